@@ -1,0 +1,171 @@
+/*
+ * Oracle for exact scaled-dot-product attention, fp64, CPU only.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg may build, load or call this file. The product path (the
+ * HIP library) never touches it, and this file shares no code, header, table
+ * or constant with that library.
+ *
+ * What it computes is the plain definition of softmax attention, one query
+ * row at a time, with the whole row of scores held in memory:
+ *   - "Standard attention" as the cookbook notebook's SDPA reference layer
+ *     computes it (hassan11196 llm-systems-cookbook, "FlashAttention-2 in an
+ *     attention layer": shape algebra section and the SDPAAttention layer),
+ *     the result FlashAttention-2 reaches exactly ("no algorithmic change --
+ *     same math", infra.bea.ai FlashAttention V2 guide, introduction).
+ *   - The score of key j for query i is scale * (q_i . k_j), the scale applied
+ *     after the dot product and before masking (cookbook Triton kernel body).
+ *   - Causal masking keeps key j for query i iff j <= i (cookbook Triton kernel,
+ *     the offs_m >= cur_n mask; queries and keys have the same length).
+ *   - Softmax is the two-pass form: m = max_j s_j, e_j = exp(s_j - m),
+ *     l = sum_j e_j; o_i = (sum_j e_j v_j) / l.
+ *   - lse_i = m + log(l), natural log (the per-row logsumexp that the
+ *     FlashAttention-2 epilogue writes, jared-hpc Lecture 6 reading task;
+ *     m and l are the running max and sum of the online softmax in the
+ *     infra.bea.ai guide, "Optimization 2: Delay Rescaling").
+ *
+ * Inputs are the exact fp64 values the GPU receives (fp16/bf16 widened by the
+ * caller). Every sum runs in a fixed order with one fp64 accumulator; the
+ * file is compiled without -ffast-math, so exp and log are libm's.
+ *
+ * Layout: q, k, v, o are contiguous (B, H, S, D) row-major: element
+ * (b, h, s, d) sits at ((b*H + h)*S + s)*D + d. lse is contiguous (B, H, S).
+ */
+#include <math.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One output row: query row i of head (b, h). `scores` holds S doubles. */
+static void oracle_one_row(const double *q, const double *k, const double *v,
+                           long H, long S, long D, long b, long h, long i,
+                           int causal, double scale, double *scores,
+                           double *o_row, double *lse_out) {
+    const long head = (b * H + h) * S * D;
+    const double *qi = q + head + i * D;
+    const long n_keys = causal ? i + 1 : S; /* keys j in [0, n_keys) */
+
+    /* scores s_j = scale * (q_i . k_j) */
+    for (long j = 0; j < n_keys; ++j) {
+        const double *kj = k + head + j * D;
+        double dot = 0.0;
+        for (long d = 0; d < D; ++d) dot += qi[d] * kj[d];
+        scores[j] = scale * dot;
+    }
+
+    /* pass 1: row max */
+    double m = -INFINITY;
+    for (long j = 0; j < n_keys; ++j)
+        if (scores[j] > m) m = scores[j];
+
+    /* pass 2: e_j = exp(s_j - m), l = sum e_j (e_j kept in `scores`) */
+    double l = 0.0;
+    for (long j = 0; j < n_keys; ++j) {
+        scores[j] = exp(scores[j] - m);
+        l += scores[j];
+    }
+
+    /* o_i = sum_j e_j v_j / l */
+    for (long d = 0; d < D; ++d) o_row[d] = 0.0;
+    for (long j = 0; j < n_keys; ++j) {
+        const double *vj = v + head + j * D;
+        const double e = scores[j];
+        for (long d = 0; d < D; ++d) o_row[d] += e * vj[d];
+    }
+    for (long d = 0; d < D; ++d) o_row[d] /= l;
+
+    *lse_out = m + log(l);
+}
+
+static int oracle_check_args(const void *q, const void *k, const void *v,
+                             const void *o, const void *lse, long B, long H,
+                             long S, long D) {
+    if (!q || !k || !v || !o || !lse) return 1;
+    if (B < 1 || H < 1 || S < 1 || D < 1) return 2;
+    return 0;
+}
+
+/*
+ * Full attention: o (B, H, S, D) and lse (B, H, S), fp64.
+ * Returns 0 on success, 1 for a null pointer, 2 for a non-positive size,
+ * 3 when the per-thread score buffer cannot be allocated.
+ */
+int oracle_attention_f64(const double *q, const double *k, const double *v,
+                         double *o, double *lse, long B, long H, long S,
+                         long D, int causal, double scale, int nthreads) {
+    int err = oracle_check_args(q, k, v, o, lse, B, H, S, D);
+    if (err) return err;
+    const long n_rows = B * H * S;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+#endif
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!scores) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 16)
+#endif
+            for (long r = 0; r < n_rows; ++r) {
+                const long i = r % S, bh = r / S;
+                oracle_one_row(q, k, v, H, S, D, bh / H, bh % H, i, causal,
+                               scale, scores, o + r * D, lse + r);
+            }
+            free(scores);
+        }
+    }
+    return failed ? 3 : 0;
+}
+
+/*
+ * Selected rows only: rows[t] is a flat row index (b*H + h)*S + i. Writes
+ * o_rows (n_rows, D) and lse_rows (n_rows). Same return codes as above, plus
+ * 4 when a row index is out of range.
+ */
+int oracle_attention_rows_f64(const double *q, const double *k,
+                              const double *v, const long *rows, long n_rows,
+                              double *o_rows, double *lse_rows, long B, long H,
+                              long S, long D, int causal, double scale,
+                              int nthreads) {
+    int err = oracle_check_args(q, k, v, o_rows, lse_rows, B, H, S, D);
+    if (err) return err;
+    if (n_rows < 0 || (n_rows > 0 && !rows)) return 1;
+    for (long t = 0; t < n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= B * H * S) return 4;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+#endif
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!scores) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+            for (long t = 0; t < n_rows; ++t) {
+                const long r = rows[t], i = r % S, bh = r / S;
+                oracle_one_row(q, k, v, H, S, D, bh / H, bh % H, i, causal,
+                               scale, scores, o_rows + t * D, lse_rows + t);
+            }
+            free(scores);
+        }
+    }
+    return failed ? 3 : 0;
+}
+
+/* Number of threads an OpenMP region would use by default (1 without OpenMP). */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

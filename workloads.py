@@ -1,0 +1,116 @@
+"""Seeded synthetic attention workloads.
+
+This module only draws inputs and names shapes. It holds none of the
+attention arithmetic, so both the HIP path's tests and the CPU oracle can take
+their inputs from here without sharing any computation.
+
+Inputs follow the pages' benchmark setting: random N(0, 1) Q, K, V in
+(batch, heads, seq, head_dim) layout, fp16 or bf16, scale 1/sqrt(head_dim)
+(jared-hpc Lecture 6 benchmark task: B=2, H=16, fp16, causal, seqlen
+512..16384, head_dim 64/128; cookbook notebook: B=1, H=32, T=2048, D=128).
+
+Recipe: a CPU torch.Generator seeded with `seed` draws q, k, v in that order
+as fp32 N(0, 1) tensors of shape (B, H, S, D); when `qk_mult` is not 1, q and
+k are multiplied by it in fp32; each tensor is then rounded once to the
+working dtype (round to nearest even). The oracle receives exactly those
+rounded values, widened to fp64.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import torch
+
+DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: str  # "f16" or "bf16"
+    causal: bool
+    qk_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    @property
+    def flops(self) -> float:
+        """4*B*H*S^2*D, halved under causal masking (the benchmark's count)."""
+        f = 4.0 * self.B * self.H * self.S * self.S * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O written once (2 B per element), lse (4 B per row)."""
+        n = self.B * self.H * self.S
+        return 4 * n * self.D * 2 + n * 4
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+def make_qkv(w: Workload, seed: int = 0):
+    """Draw (q, k, v) on the CPU in the workload's dtype (see module recipe)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (w.B, w.H, w.S, w.D)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.qk_mult != 1.0:
+        q = q * w.qk_mult
+        k = k * w.qk_mult
+    dt = w.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+# Tiny exact case: B=1, H=2, S=256, D=64, fp16, causal and non-causal.
+TINY = [
+    Workload("tiny_causal", 1, 2, 256, 64, "f16", True),
+    Workload("tiny_noncausal", 1, 2, 256, 64, "f16", False),
+]
+
+# Sequence-length x head-dim sweep: B=2, H=16, fp16, causal.
+SWEEP = [
+    Workload(f"sweep_s{S}_d{D}", 2, 16, S, D, "f16", True)
+    for D in (64, 128)
+    for S in (512, 1024, 2048, 4096, 8192, 16384)
+]
+
+# The headline point of the sweep.
+HEADLINE = Workload("sweep_s8192_d128", 2, 16, 8192, 128, "f16", True)
+
+# LLM-layer shape: B=1, H=32, S=2048, D=128, fp16, causal and non-causal.
+LLM_LAYER = [
+    Workload("llm_layer_causal", 1, 32, 2048, 128, "f16", True),
+    Workload("llm_layer_noncausal", 1, 32, 2048, 128, "f16", False),
+]
+
+# Long-sequence, low-parallelism prefill: bf16, Q and K scaled x3 (peaky rows).
+LONG_PREFILL = Workload("long_prefill", 1, 8, 16384, 128, "bf16", False, qk_mult=3.0)
+
+# Ragged large head dim: S = 4097 is not a tile multiple, D = 256, bf16 causal.
+RAGGED_D256 = Workload("ragged_d256", 4, 16, 4097, 256, "bf16", True)
+
+ALL = TINY + SWEEP + LLM_LAYER + [LONG_PREFILL, RAGGED_D256]
+
+TOLERANCE_O = {"f16": 2e-3, "bf16": 1.6e-2}
+TOLERANCE_LSE_REL = 1e-4
+
+
+def by_name(name: str) -> Workload:
+    for w in ALL:
+        if w.name == name:
+            return w
+    raise KeyError(name)
