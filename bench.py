@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention-2 forward pass on one MI355X.
+
+One step is one fa2_fwd launch over the whole workload (inputs already
+resident in HBM). Default workload: B=2, H=16, S=8192, D=128, fp16, causal.
+Prints one JSON line on stdout; diagnostics go to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --table PATH      # every benchmark shape, one line each
+
+Metric: TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal masking, and the
+fraction of the MI355X dense fp16/bf16 matrix-core peak (256 CUs x 2.4 GHz x
+4096 FLOP/clk/CU = 2516.6 TFLOP/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "flashattention_tiled_amd", "csrc", "fa2_fwd.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa2_fwd_kernel_sweep_s8192_d128_counters.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on this workload with the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    fields = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", text, flags=re.M))
+    if fields.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    if fields.get("workload") != workload_name:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import flashattention_tiled_amd as fa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    q, k, v = wl.make_qkv(w, seed=0)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dtype = fa.FA2_F16 if w.dtype == "f16" else fa.FA2_BF16
+    lib = fa.load_library()
+    args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.S, w.D, int(w.causal), float(w.scale), dtype, stream.cuda_stream)
+
+    def launch():
+        st = lib.fa2_fwd(*args)
+        if st != 0:
+            raise fa.FA2Error(st, fa.fa2_status_string(st))
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize(dev)
+
+    # per-launch HIP events on the launch stream, plus wall clock over the steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
+    return dict(q=q, k=k, v=v, o=o, lse=lse, wall_s=wall, durs_ms=durs)
+
+
+def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
+    """Time the fp64 oracle on a random sample of rows of the same workload
+    (about `budget_s` of CPU work) and compare those rows with the GPU output."""
+    import numpy as np
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    rng = np.random.default_rng(0)
+    n_rows_total = w.B * w.H * w.S
+
+    def row_flops(rows):
+        i = rows % w.S
+        keys = (i + 1) if w.causal else np.full_like(i, w.S)
+        return float((4.0 * keys * w.D).sum())
+
+    # calibrate on growing samples until one takes >= 0.5 s, then size the
+    # timed sample to the budget
+    m = 64
+    while True:
+        probe = rng.integers(0, n_rows_total, size=min(m, n_rows_total))
+        t0 = time.perf_counter()
+        oracle.attention_rows_f64(qn, kn, vn, probe, w.causal, w.scale, nthreads=cores)
+        t = time.perf_counter() - t0
+        if t >= 0.5 or m >= n_rows_total:
+            break
+        m *= 4
+    per_flop = t / row_flops(probe)
+    mean_row_flops = 4.0 * w.D * ((w.S + 1) / 2 if w.causal else w.S)
+    n = int(min(n_rows_total, max(cores, budget_s / (per_flop * mean_row_flops))))
+    rows = np.sort(rng.choice(n_rows_total, size=n, replace=False))
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attention_rows_f64(qn, kn, vn, rows, w.causal, w.scale,
+                                               nthreads=cores)
+    dt = time.perf_counter() - t0
+    flops = row_flops(rows)
+    og = o_gpu.reshape(-1, w.D).cpu()[rows].double().numpy()
+    lg = lse_gpu.reshape(-1).cpu()[rows].double().numpy()
+    o_err = float(np.abs(og - o_ref).max())
+    lse_err = float((np.abs(lg - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max())
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=(f"{n} of {n_rows_total} query rows drawn uniformly (seed 0), "
+                        f"{flops:.3e} FLOPs in {dt:.1f} s, fp64, {cpu}"),
+                seconds=dt, parity_max_abs_o=o_err, parity_lse_rel=lse_err)
+
+
+def stats_line(w, r):
+    durs = r["durs_ms"]
+    avg = sum(durs) / len(durs)
+    med = durs[len(durs) // 2]
+    return avg, med
+
+
+def run_table(path: str, steps: int, warmup: int):
+    import workloads as wl
+
+    rows = []
+    for w in wl.ALL:
+        r = time_gpu(w, steps, warmup)
+        avg, med = stats_line(w, r)
+        tf = w.flops / (med * 1e-3) / 1e12
+        gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9
+        line = (f"{w.name},{w.B},{w.H},{w.S},{w.D},{w.dtype},{int(w.causal)},"
+                f"{med:.4f},{avg:.4f},{min(r['durs_ms']):.4f},{tf:.1f},"
+                f"{100 * tf / PEAK_TFLOPS:.2f},{gbs:.1f}")
+        log(line)
+        rows.append(line)
+        del r
+    with open(path, "w") as f:
+        f.write("workload,B,H,S,D,dtype,causal,ms_median,ms_avg,ms_min,tflops,pct_peak,alg_GBps\n")
+        f.write("\n".join(rows) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="sweep_s8192_d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--table", default=None, help="time every benchmark shape into a CSV")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (`steps` times), to "
+                         "calibrate the HBM byte counters against a known traffic")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the forward pass on one GPU only; "
+              "runs on more than one GPU are not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flashattention_tiled_amd as fa
+    import workloads as wl
+
+    fa.load_library()  # fails loudly when the HIP library is missing
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.table:
+        run_table(args.table, args.steps, args.warmup)
+        return
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x {args.steps} (reads {n} B and writes {n} B per copy)")
+        return
+
+    w = wl.by_name(args.workload)
+    log(f"[bench] {w} steps={args.steps} warmup={args.warmup}")
+    r = time_gpu(w, args.steps, args.warmup)
+    avg, med = stats_line(w, r)
+    ms_per_step = 1e3 * r["wall_s"] / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (avg * 1e-3) / 1e12
+    log(f"[bench] kernel avg {avg:.4f} ms, median {med:.4f} ms, min {r['durs_ms'][0]:.4f} ms, "
+        f"max {r['durs_ms'][-1]:.4f} ms; wall {ms_per_step:.4f} ms/step")
+    traffic = read_traffic(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, r["q"], r["k"], r["v"], r["o"], r["lse"], args.cpu_budget)
+        log(f"[bench] oracle sample: {cpu['sample']}; parity max|dO|={cpu['parity_max_abs_o']:.3e} "
+            f"lse_rel={cpu['parity_lse_rel']:.3e}")
+
+    out = {
+        "metric": "attention fwd TFLOP/s and % of fp16 MFMA peak, B=2 H=16 S=8192 D=128 causal",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "causal": w.causal, "qk_mult": w.qk_mult, "scale": w.scale,
+                   "flops_per_step": w.flops, "seed": 0},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5)},
+        "cpu_baseline": None if cpu is None else {
+            k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "parity_sample": None if cpu is None else {
+            "max_abs_o": cpu["parity_max_abs_o"], "lse_rel": cpu["parity_lse_rel"],
+            "tol_o": wl.TOLERANCE_O[w.dtype], "tol_lse_rel": wl.TOLERANCE_LSE_REL},
+        "host": platform.node(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

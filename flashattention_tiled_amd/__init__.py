@@ -1,0 +1,146 @@
+"""FlashAttention-2 forward pass for MI355X (gfx950): thin Python binding.
+
+Every step of the forward pass runs in the HIP library ``libfa2.so`` built
+from ``csrc/fa2_fwd.hip``; this module only marshals arguments to its C ABI
+(declared in ``include/fa2.h``). PyTorch is used for device memory and
+streams. There is no fallback: if the library is missing, importing the
+binding's functions raises.
+
+C entry points, re-exported under the same names:
+    fa2_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, stream) -> int
+    fa2_supported(D, dtype) -> int
+    fa2_status_string(status) -> str
+    fa2_rows_per_workgroup(D) -> int
+plus the tensor-level convenience ``attention(q, k, v, causal, scale)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa2.so")
+
+# fa2_dtype
+FA2_F16 = 0
+FA2_BF16 = 1
+
+# fa2_status
+FA2_OK = 0
+FA2_ERR_NULL = 1
+FA2_ERR_SHAPE = 2
+FA2_ERR_HEADDIM = 3
+FA2_ERR_DTYPE = 4
+FA2_ERR_ALIGN = 5
+FA2_ERR_SCALE = 6
+FA2_ERR_NO_DEVICE = 7
+FA2_ERR_LAUNCH = 8
+FA2_ERR_ALIAS = 9
+
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_supported", "fa2_status_string", "fa2_rows_per_workgroup")
+
+
+class FA2Error(RuntimeError):
+    """A nonzero fa2_status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa2 status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa2.so (once). Raises OSError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise OSError(f"{path} is missing: build it with flashattention_tiled_amd.build "
+                      f"(or __graft_entry__.build()) before use")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa2_fwd.restype = i
+    lib.fa2_supported.argtypes = [i, i]
+    lib.fa2_supported.restype = i
+    lib.fa2_status_string.argtypes = [i]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    lib.fa2_rows_per_workgroup.argtypes = [i]
+    lib.fa2_rows_per_workgroup.restype = i
+    _lib = lib
+    return lib
+
+
+def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+            causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the C entry point with raw device addresses; returns the status."""
+    return int(load_library().fa2_fwd(q, k, v, o, lse, B, H, S, D, int(causal),
+                                      float(scale), int(dtype), stream))
+
+
+def fa2_supported(D: int, dtype: int) -> int:
+    return int(load_library().fa2_supported(D, dtype))
+
+
+def fa2_status_string(status: int) -> str:
+    return load_library().fa2_status_string(status).decode()
+
+
+def fa2_rows_per_workgroup(D: int) -> int:
+    return int(load_library().fa2_rows_per_workgroup(D))
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float16:
+        return FA2_F16
+    if t.dtype == torch.bfloat16:
+        return FA2_BF16
+    return -1
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+              stream=None):
+    """O, lse = softmax(scale * q k^T [causal]) v for (B, H, S, D) CUDA tensors.
+
+    q, k, v: contiguous torch tensors on one GPU, fp16 or bf16, same shape.
+    scale defaults to 1/sqrt(D). Returns (o, lse): o like q, lse (B, H, S)
+    float32 (natural-log logsumexp per row). `out`/`lse` may be passed
+    preallocated. Runs on `stream` (default: torch's current stream) without
+    synchronising. Raises FA2Error on any nonzero status.
+    """
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError(f"q, k, v must share one (B, H, S, D) shape, got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must have one dtype")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous (B, H, S, D)")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, S) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), B, H, S, D, int(bool(causal)), float(scale),
+                         _dtype_code(q), stream.cuda_stream)
+    if status != FA2_OK:
+        raise FA2Error(status, fa2_status_string(status))
+    return out, lse

@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status before touching a device.
+
+Pointers here are plain integers that are never dereferenced: every case
+below returns during argument validation, before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_tiled_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa2_\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from flashattention_tiled_amd.build import build_library
+        build_library(force=False)
+    return fa.load_library()
+
+
+def test_header_declares_expected_functions():
+    assert sorted(_declared_functions()) == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libfa2.so does not export {name}"
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_enums_match_header():
+    text = open(HEADER).read()
+    for name, value in re.findall(r"(FA2_\w+)\s*=\s*(\d+)", text):
+        assert getattr(fa, name) == int(value), name
+
+
+def test_supported_and_rows(lib):
+    for D in (64, 128, 256):
+        for dt in (fa.FA2_F16, fa.FA2_BF16):
+            assert fa.fa2_supported(D, dt) == 1
+        assert fa.fa2_rows_per_workgroup(D) > 0
+    for D in (0, 32, 96, 512):
+        assert fa.fa2_supported(D, fa.FA2_F16) == 0
+        assert fa.fa2_rows_per_workgroup(D) == 0
+    assert fa.fa2_supported(128, 2) == 0
+
+
+def test_status_strings(lib):
+    for s in range(10):
+        assert fa.fa2_status_string(s)
+    assert fa.fa2_status_string(0) == "ok"
+    assert "unknown" in fa.fa2_status_string(99)
+
+
+# Fake, 256-byte aligned, non-overlapping addresses for a (1, 1, 64, 64) problem.
+_N = 64 * 64 * 2
+Q, K, V, O, L = (0x10000000 + i * 0x100000 for i in range(5))
+
+
+def _call(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, S=64, D=64, causal=0, scale=0.125,
+                dtype=fa.FA2_F16, stream=None)
+    args.update(kw)
+    return fa.fa2_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA2_ERR_NULL),
+    (dict(k=0), fa.FA2_ERR_NULL),
+    (dict(v=None), fa.FA2_ERR_NULL),
+    (dict(o=None), fa.FA2_ERR_NULL),
+    (dict(lse=None), fa.FA2_ERR_NULL),
+    (dict(B=0), fa.FA2_ERR_SHAPE),
+    (dict(H=0), fa.FA2_ERR_SHAPE),
+    (dict(S=0), fa.FA2_ERR_SHAPE),
+    (dict(S=-5), fa.FA2_ERR_SHAPE),
+    (dict(B=65536), fa.FA2_ERR_SHAPE),
+    (dict(H=70000), fa.FA2_ERR_SHAPE),
+    (dict(B=65535, H=65535, S=2**31 - 1, D=256), fa.FA2_ERR_SHAPE),
+    (dict(D=32), fa.FA2_ERR_HEADDIM),
+    (dict(D=96), fa.FA2_ERR_HEADDIM),
+    (dict(D=512), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA2_ERR_DTYPE),
+    (dict(dtype=-1), fa.FA2_ERR_DTYPE),
+    (dict(q=Q + 8), fa.FA2_ERR_ALIGN),
+    (dict(o=O + 2), fa.FA2_ERR_ALIGN),
+    (dict(lse=L + 2), fa.FA2_ERR_ALIGN),
+    (dict(scale=float("nan")), fa.FA2_ERR_SCALE),
+    (dict(scale=float("inf")), fa.FA2_ERR_SCALE),
+    (dict(scale=-0.5), fa.FA2_ERR_SCALE),
+    (dict(o=Q), fa.FA2_ERR_ALIAS),
+    (dict(o=K + 16), fa.FA2_ERR_ALIAS),
+    (dict(lse=V + _N - 4), fa.FA2_ERR_ALIAS),
+    (dict(lse=O + 64), fa.FA2_ERR_ALIAS),
+])
+def test_validation_status(lib, kw, status):
+    assert _call(**kw) == status
+
+
+def test_validation_happens_before_device_lookup(lib):
+    # Errors in several arguments report the first check in documented order
+    # and never reach the device: no GPU is needed to get them.
+    assert _call(q=None, D=3) == fa.FA2_ERR_NULL
+    assert _call(S=0, D=3) == fa.FA2_ERR_SHAPE
+
+
+def test_attention_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.attention(x, x, x)
+    with pytest.raises(ValueError):
+        fa.attention(x, x, x[:, :, :4])
+
+
+def test_no_device_status_without_gpu(lib):
+    """On a host with no GPU a fully valid call reports FA2_ERR_NO_DEVICE.
+    (Skipped where a GPU exists: these fake addresses must never reach a kernel.)"""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call() == fa.FA2_ERR_NO_DEVICE

@@ -1,0 +1,104 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Tolerances (written here, applied to every case): max |O_gpu - O_ref| <= 2e-3
+for fp16 output and <= 1.6e-2 for bf16 output; lse relative error
+|lse_gpu - lse_ref| / max(|lse_ref|, 1) <= 1e-4.
+
+Small sizes compare every output; the full benchmark shapes compare sampled
+rows (edges, tile boundaries, the ragged tail, random rows) that the oracle
+computes one by one, in the same launch configuration the bench times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_helpers import (announce, assert_parity, oracle_full, oracle_rows, run_gpu,
+                         sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# the tiny exact configuration, every output, three seeds
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("w", wl.TINY, ids=lambda w: w.name)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_full(w, seed):
+    announce(f"tiny {w} seed={seed}")
+    q, k, v = wl.make_qkv(w, seed)
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    o_ref, lse_ref = oracle_full(q, k, v, w.causal, w.scale)
+    assert_parity(o, lse, o_ref, lse_ref, w.dtype, f"{w.name} seed {seed}")
+
+
+# ---------------------------------------------------------------------------
+# small shapes spanning several tiles and ragged tails, every output
+# ---------------------------------------------------------------------------
+SMALL_S = [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 257, 383]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_small_shapes_full(D, dtype, causal):
+    for S in SMALL_S:
+        w = wl.Workload(f"small_S{S}", 1, 2, S, D, dtype, causal)
+        announce(f"small {w}")
+        q, k, v = wl.make_qkv(w, seed=S)
+        o, lse = run_gpu(q, k, v, causal, w.scale)
+        o_ref, lse_ref = oracle_full(q, k, v, causal, w.scale)
+        assert_parity(o, lse, o_ref, lse_ref, dtype, w.name + f" D{D} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_batch_heads_full(dtype):
+    """Several batches and heads with a ragged S: every (b, h) slice is checked."""
+    for causal in (False, True):
+        w = wl.Workload("multi_bh", 3, 5, 301, 128, dtype, causal)
+        announce(f"multi {w}")
+        q, k, v = wl.make_qkv(w, seed=7)
+        o, lse = run_gpu(q, k, v, causal, w.scale)
+        o_ref, lse_ref = oracle_full(q, k, v, causal, w.scale)
+        assert_parity(o, lse, o_ref, lse_ref, dtype, f"multi_bh causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_peaky_small_full(dtype):
+    """Q and K scaled x3 (peaky softmax rows), as in the long-prefill workload."""
+    w = wl.Workload("peaky", 1, 4, 700, 128, dtype, False, qk_mult=3.0)
+    announce(f"peaky {w}")
+    q, k, v = wl.make_qkv(w, seed=3)
+    o, lse = run_gpu(q, k, v, False, w.scale)
+    o_ref, lse_ref = oracle_full(q, k, v, False, w.scale)
+    assert_parity(o, lse, o_ref, lse_ref, dtype, "peaky small")
+
+
+def test_scale_values():
+    """Scale 0 (uniform weights), a large scale, and a non-default value."""
+    for scale in (0.0, 0.5, 1.0 / 3.0):
+        w = wl.Workload("scales", 1, 2, 190, 64, "f16", True)
+        announce(f"scale={scale} {w}")
+        q, k, v = wl.make_qkv(w, seed=5)
+        o, lse = run_gpu(q, k, v, True, scale)
+        o_ref, lse_ref = oracle_full(q, k, v, True, scale)
+        assert_parity(o, lse, o_ref, lse_ref, "f16", f"scale {scale}")
+
+
+# ---------------------------------------------------------------------------
+# the benchmark shapes at full size, sampled rows
+# ---------------------------------------------------------------------------
+FULL = wl.SWEEP + wl.LLM_LAYER + [wl.LONG_PREFILL, wl.RAGGED_D256]
+
+
+@pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
+def test_full_size_sampled(w):
+    announce(f"full-size {w}")
+    q, k, v = wl.make_qkv(w, seed=0)
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rows = sample_rows(w.B, w.H, w.S)
+    o_ref, lse_ref = oracle_rows(q, k, v, rows, w.causal, w.scale)
+    o_s = o.reshape(-1, w.D)[torch.from_numpy(rows)]
+    lse_s = lse.reshape(-1)[torch.from_numpy(rows)]
+    assert_parity(o_s, lse_s, o_ref, lse_ref, w.dtype, f"{w.name} ({len(rows)} rows)")
