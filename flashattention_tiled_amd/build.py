@@ -11,10 +11,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU instructions are disabled for all device code.
+# Packed fp32 VALU instructions are disabled for all device code. Matrix-core
+# results are kept in VGPRs (not AGPRs): the online softmax rescales the
+# output accumulator in place, and in the AGPR form the compiler copies the
+# whole accumulator out and back on every loop iteration.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

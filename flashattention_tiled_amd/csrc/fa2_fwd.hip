@@ -3,37 +3,60 @@
 // One workgroup owns a tile of B_r query rows of one (batch, head); the grid
 // is (ceil(S / B_r), H, B), the sequence-parallel grid of FlashAttention-2
 // (jared-hpc Lecture 6, "FA2 change 1"). Inside the workgroup every 64-lane
-// wavefront owns 32 query rows outright and runs the whole key loop on them,
+// wavefront owns its query rows outright and runs the whole key loop on them,
 // so waves never exchange softmax state (infra.bea.ai FlashAttention V2 guide,
 // "Optimization 3: Warp-Level Work Partitioning", split-Q). K and V tiles of
-// B_c keys are staged in LDS once per workgroup and read by all its waves.
+// B_c keys stream through a ring of LDS stages shared by the workgroup's
+// waves; the next tiles are in flight while the current one is computed.
 //
-// Per key tile j the wave computes (infra.bea.ai guide, "Optimization 2:
-// Delay Rescaling"; the cookbook notebook's Triton kernel loop):
-//   S   = Q K_j^T                              (matrix cores, fp32 accumulate)
-//   m'  = max(m, rowmax(c * S)),  c = scale * log2(e)
-//   P   = 2^(c * S - m'),  alpha = 2^(m - m')
-//   l   = alpha * l + rowsum(P)
-//   O~  = alpha * O~ + P V_j                   (matrix cores, P rounded to the
-//                                               input dtype, fp32 accumulate)
+// Per key tile j a wave computes, for each query row it owns (infra.bea.ai
+// guide, "Optimization 2: Delay Rescaling"; the cookbook notebook's Triton
+// kernel loop):
+//   S   = Q K_j^T                         (matrix cores, fp32 accumulate)
+//   t   = c * S,  c = scale * log2(e)     (base-2 logits)
+//   P   = 2^(t - m)                       rounded to the input dtype
+//   l   = l + rowsum(P)
+//   O~  = O~ + P V_j                      (matrix cores, fp32 accumulate)
 // and only the epilogue divides by l and writes lse = ln2 * (m + log2 l).
-// Base-2 exponentials with scale*log2(e) folded into one FMA give the same
-// values as exp(scale*S - m) since 2^(x log2 e) = e^x.
+// 2^(x log2 e) = e^x, so these are the pages' exp-based recurrences.
+//
+// The reference point m is the running row max, moved lazily: it is raised
+// (rescaling O~ and l by alpha = 2^(m_old - m_new), as the guide's
+// recurrence does) only when a tile's max exceeds it by more than kTau = 8.
+// Any m at or above the true running max minus kTau gives the same O and
+// lse exactly -- it cancels between O~ and l -- while P stays <= 2^8, far
+// inside fp16/bf16 range. l sums the *rounded* P that the P V product uses,
+// so O is an exact convex combination of V rows whatever the rounding of P.
 //
 // Matrix-core formulation. The wave computes the transposed products
-//   S^T = K_j Q^T   (A = K_j from LDS,  B = Q^T resident in registers)
+//   S^T = K_j Q^T   (A = K_j from LDS,   B = Q^T resident in registers)
 //   O^T = V_j^T P^T (A = V_j^T from LDS, B = P^T straight from S^T's registers)
 // with v_mfma_f32_32x32x16_{f16,bf16}. Output column n of a 32x32 block lives
-// in lane n (mod 32), so each lane holds one query row: the row max and row
-// sum need only in-lane reductions plus one exchange with the lane 32 away,
-// and the per-row rescale by alpha is a per-lane scalar multiply.
+// in lane n (mod 32), so each lane holds one query row per 32-row block: the
+// row max and row sum are in-lane reductions plus one exchange with the lane
+// 32 away, and the per-row rescale is a per-lane scalar multiply.
 //
 // MFMA 32x32x16 lane layouts used below (lane l, l32 = l % 32, hi = l / 32):
-//   A (32 x 16): lane l holds row l32, 8 consecutive k values of half hi.
+//   A (32 x 16): lane l holds row l32, 8 k values of half hi.
 //   B (16 x 32): lane l holds column l32, the same 8 k values.
 //   C (32 x 32): register r of lane l holds row 8*(r/4) + 4*hi + r%4, column l32.
 // Any bijection between (hi, element) and k is valid as long as A and B use
-// the same one, which is how P^T is fed from the S^T accumulator registers.
+// the same one, which is how P^T is fed from the S^T accumulator registers:
+// B element e of P^T step (kb, h) is accumulator register 8h + e, that is
+// key 32 kb + 16 h + 8 (e / 4) + 4 hi + e % 4, and the V^T operand gathers
+// the same keys.
+//
+// LDS staging. Tiles arrive by buffer loads that write LDS directly, 16 bytes
+// per lane; a 64-lane load fills 1 KiB of consecutive 16-byte slots, so the
+// layout is chosen by which global chunk each lane fetches. Key rows are
+// row-major with their 16-byte chunks XOR-swizzled per row so that the reads
+// below hit distinct banks. Buffer loads past the end of a head return zero,
+// which zero-fills the keys beyond S of a ragged last tile.
+//   K^T A operand: one 16-byte read of row key, chunk (2 s + hi).
+//   V^T A operand: two ds_read_b64_tr_b16, the gfx950 transposing read. In
+//   each 16-lane group, output lane i element e comes from source lane
+//   4 e + i / 4, element i % 4; sources pointed at 4 key rows x 16 dims return
+//   4 consecutive keys of one dim per lane, the layout the A operand needs.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -52,12 +75,20 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (base-2 units)
 
-// Element-type specific pieces: the matrix-core product and the RNE packing
-// of two fp32 values into the input dtype.
+// Buffer resource word 3 for raw (unswizzled, stride 0) buffers on gfx9.
+constexpr int kBufferFlags = 0x00020000;
+
+// Element-type specific pieces: the matrix-core product, the RNE packing of
+// two fp32 values into the input dtype, and the sum of a packed pair.
 template <int DT> struct Elem;
 
 template <> struct Elem<FA2_F16> {
@@ -68,6 +99,11 @@ template <> struct Elem<FA2_F16> {
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     f16x2 h = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, h);
+  }
+  // acc + lo + hi of a packed pair, in fp32
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
   }
 };
 
@@ -80,44 +116,129 @@ template <> struct Elem<FA2_BF16> {
     bf16x2 h = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, h);
   }
+  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
+  }
 };
 
 // Tile shape per head dimension.
-template <int D> struct Tile {
-  static constexpr int kWaves = 4;             // waves per workgroup
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRowsPerWave = 32;      // query rows owned by one wave
-  static constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
-  static constexpr int kBc = 64;               // keys per tile
-  static constexpr int kKPitch = D + 8;        // K tile row pitch in LDS (elements)
-  static constexpr int kVPitch = kBc + 4;      // V^T tile row pitch in LDS (elements)
-  // Waves per SIMD the register budget is sized for: two at D <= 128 (256
-  // VGPRs each), one at D = 256 (O~ alone takes 128 registers per lane).
-  static constexpr int kMinWavesPerSimd = D <= 128 ? 2 : 1;
+//   kRowBlocks  32-row MFMA blocks per wave (each K/V fragment read from LDS
+//               feeds kRowBlocks MFMAs, so more blocks mean fewer LDS bytes
+//               per FLOP, at the cost of registers)
+//   kBc         keys per tile;  kStages  LDS ring depth
+//   kWavesPerSimd  waves per SIMD the register budget is sized for
+template <int D> struct Tile;
+template <> struct Tile<64> {
+  static constexpr int kRowBlocks = 2, kBc = 64, kStages = 3, kWavesPerSimd = 1;
+};
+template <> struct Tile<128> {
+  static constexpr int kRowBlocks = 2, kBc = 32, kStages = 4, kWavesPerSimd = 2;
+};
+template <> struct Tile<256> {
+  static constexpr int kRowBlocks = 1, kBc = 64, kStages = 2, kWavesPerSimd = 1;
 };
 
-// Value of x held by the lane 32 away, combined with x by max or by sum.
-__device__ __forceinline__ float max_with_other_half(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+template <int D> struct Shape {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRB = Tile<D>::kRowBlocks;
+  static constexpr int kRowsPerWave = 32 * kRB;
+  static constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
+  static constexpr int kBc = Tile<D>::kBc;
+  static constexpr int kStages = Tile<D>::kStages;
+  static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per key row
+  static constexpr int kTileBytes = kBc * D * 2;     // one K or one V tile
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per K (or V) tile
+  static constexpr int kLdsBytes = kStages * 2 * kTileBytes;
+  static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+// Chunk swizzles (XOR on the 16-byte chunk index within a key row).
+__device__ __forceinline__ int swz_k(int row) { return row & 7; }
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+
+// s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding; expcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
-__device__ __forceinline__ float sum_with_other_half(float x) {
-  return x + __shfl_xor(x, 32);
+
+// Wait until at most PER * n vector-memory loads are outstanding, n <= MAXN
+// known only at run time (s_waitcnt takes an immediate).
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_for_tile(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vm_lgkm0<0>();
+  } else {
+    if (n >= MAXN)
+      wait_vm_lgkm0<PER * MAXN>();
+    else
+      wait_for_tile<PER, MAXN - 1>(n);
+  }
+}
+
+__device__ __forceinline__ void workgroup_barrier() {
+  __asm__ volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Start the loads of one K tile and one V tile into LDS stage `st`: this
+// wave's LPW 1 KiB blocks of each, from byte `base` of the head (tile t
+// starts at t * TB since a tile is Bc whole key rows). LDS slot
+// p = block * 64 + lane receives chunk (p % CPR) ^ swz(row) of key row p / CPR.
+template <int D, int LPW, int TB>
+__device__ __forceinline__ void issue_tile(unsigned char* smem, int wave, int lane,
+                                           __amdgpu_buffer_rsrc_t k_rsrc,
+                                           __amdgpu_buffer_rsrc_t v_rsrc, uint32_t base,
+                                           int st) {
+  constexpr int CPR = D / 8;
+  unsigned char* kst = smem + st * 2 * TB;
+  unsigned char* vst = kst + TB;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int p = (wave * LPW + i) * 64 + lane;
+    const int r = p / CPR, cp = p % CPR;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(kst + (wave * LPW + i) * 1024),
+                                             16, base + (uint32_t)((r * D + (cp ^ swz_k(r)) * 8) * 2),
+                                             0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int p = (wave * LPW + i) * 64 + lane;
+    const int r = p / CPR, cp = p % CPR;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(vst + (wave * LPW + i) * 1024),
+                                             16, base + (uint32_t)((r * D + (cp ^ swz_v(r)) * 8) * 2),
+                                             0, 0, 0);
+  }
 }
 
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kMinWavesPerSimd) void fa2_fwd_kernel(
+__global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int S, float c /* scale * log2(e) */) {
-  using T = Tile<D>;
+  using SH = Shape<D>;
   using E = Elem<DT>;
-  constexpr int Bc = T::kBc, Br = T::kBr, KP = T::kKPitch, VP = T::kVPitch;
+  constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr, NS = SH::kStages;
+  constexpr int CPR = SH::kChunksPerRow, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
   constexpr int NKB = Bc / 32;  // 32-key blocks per tile
   constexpr int NDS = D / 16;   // k-steps of 16 over the head dim (S^T product)
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O^T
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[Bc * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VP];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SH::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -125,8 +246,8 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kMinWavesPerSimd) void 
 
   // Workgroup -> (query tile, batch*head). Tiles are taken in descending
   // query-tile order across all heads, so under causal masking the longest
-  // tiles start first; consecutive workgroups of one (b, h) are H*B apart in
-  // launch order, which keeps them on one XCD when H*B is a multiple of 8.
+  // tiles start first; the workgroups of one (b, h) are H*B apart in launch
+  // order, which keeps them on one XCD when H*B is a multiple of 8.
   const int n_qt = gridDim.x;
   const int n_bh = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -134,168 +255,227 @@ __global__ __launch_bounds__(Tile<D>::kThreads, Tile<D>::kMinWavesPerSimd) void 
   const int qt = n_qt - 1 - lin / n_bh;
   const int q0 = qt * Br;
   const size_t head = (size_t)bh * (size_t)S * D;
+  const int wave_row0 = q0 + wave * SH::kRowsPerWave;
 
-  const int wave_row0 = q0 + wave * T::kRowsPerWave;
-  const int row = wave_row0 + l32;  // the query row this lane owns
-
-  // Q^T operand: lane holds Q[row][16 s + 8 hi .. +7] for every k-step s.
-  u32x4 qf[NDS];
+  // Q^T operands: lane holds Q[row][16 s + 8 hi .. +7] of each of its rows.
+  u32x4 qf[RB][NDS];
 #pragma unroll
-  for (int s = 0; s < NDS; ++s) {
-    qf[s] = u32x4{0, 0, 0, 0};
-    if (row < S) qf[s] = *(const u32x4*)(q + head + (size_t)row * D + 16 * s + 8 * hi);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave_row0 + 32 * rb + l32;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      qf[rb][s] = u32x4{0, 0, 0, 0};
+      if (row < S) qf[rb][s] = *(const u32x4*)(q + head + (size_t)row * D + 16 * s + 8 * hi);
+    }
   }
 
-  f32x16 acc_o[NDB];
+  // K and V of this head as bounds-checked byte buffers.
+  const uint32_t head_bytes = (uint32_t)S * D * 2;
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(k + head), 0, (int)head_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(v + head), 0, (int)head_bytes, kBufferFlags);
+
+  // LDS read offsets that do not depend on the tile.
+  // K^T operand: row 32 kb + l32, chunk (2 s + hi) ^ (l32 & 7).
+  const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ (l32 & 7)));
+  // V^T operand: row 32 kb + 16 h + 4 hi + (lane % 16) / 4 (+8 for e >= 4),
+  // dims 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3, i.e. chunk
+  // 4 db + vt_chunk, byte 8 (lane % 2) within it. The swizzle XORs bits 1-2
+  // of the chunk index; bit 2 is bit 0 of db, so even and odd db blocks get
+  // their own base: chunk (4 db + c) ^ w = 4 (db ^ (w >> 2)) + (c ^ (w & 3)).
+  const int vt_row = 4 * hi + (lane & 15) / 4;
+  const int vt_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vt_w = swz_v(vt_row);
+  const int vt_common = (vt_row * CPR + (vt_chunk ^ (vt_w & 3))) * 16 + 8 * (lane & 1);
+  const int vt_even = vt_common + 64 * (vt_w >> 2);  // db even: 4 (db ^ b) = 4 db + 4 b
+  const int vt_odd = vt_common - 64 * (vt_w >> 2);   // db odd:  4 (db ^ b) = 4 db - 4 b
+
+  f32x16 acc_o[RB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of c*S (base-2 units)
-  float l_run = 0.f;        // this lane's share of the running sum
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc_o[rb][db] = f32x16{};
+  // Per row (this lane's share of its keys): the reference max m of t
+  // (base-2), the sum of P as computed (for lse), and the sum of P as
+  // rounded for the P V product (normalises O).
+  float m_run[RB], l_run[RB], l_rnd[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+    l_rnd[rb] = 0.f;
+  }
 
   const int kv_end = CAUSAL ? min(q0 + Br, S) : S;
   const int n_tiles = (kv_end + Bc - 1) / Bc;
 
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < n_tiles) issue_tile<D, LPW, TB>(smem, wave, lane, k_rsrc, v_rsrc, (uint32_t)t * TB, t);
+
   for (int j = 0; j < n_tiles; ++j) {
+    // This wave's loads of tile j are done (those of the tiles after it that
+    // are already issued may still be in flight); after the barrier every
+    // wave's are, and every wave has finished reading tile j - 1, whose stage
+    // is refilled next.
+    wait_for_tile<2 * LPW, NS - 2>(min(NS - 2, n_tiles - 1 - j));
+    workgroup_barrier();
+    if (j + NS - 1 < n_tiles)
+      issue_tile<D, LPW, TB>(smem, wave, lane, k_rsrc, v_rsrc, (uint32_t)(j + NS - 1) * TB,
+                             (j + NS - 1) % NS);
+
     const int key0 = j * Bc;
-    __syncthreads();  // every wave is done reading the previous tile
-
-    // K tile, row-major [key][d]; keys >= S are zero.
-    constexpr int kChunks = Bc * D / 8;  // 16-byte chunks
-#pragma unroll
-    for (int ci = tid; ci < kChunks; ci += T::kThreads) {
-      const int r = ci / (D / 8), c8 = ci % (D / 8);
-      u32x4 val = {0, 0, 0, 0};
-      if (key0 + r < S) val = *(const u32x4*)(k + head + (size_t)(key0 + r) * D + c8 * 8);
-      *(u32x4*)(k_lds + r * KP + c8 * 8) = val;
-    }
-    // V tile, transposed to [d][key]: a thread loads 4 keys x 8 dims and
-    // writes 8 rows of 4 keys.
-    constexpr int kVGroups = (Bc / 4) * (D / 8);
-#pragma unroll
-    for (int g = tid; g < kVGroups; g += T::kThreads) {
-      const int kq = g / (D / 8), dc = g % (D / 8);
-      u32x4 x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 4 * kq + r;
-        x[r] = u32x4{0, 0, 0, 0};
-        if (key < S) x[r] = *(const u32x4*)(v + head + (size_t)key * D + dc * 8);
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 even = {(x[0][w] & 0xffffu) | (x[1][w] << 16),
-                            (x[2][w] & 0xffffu) | (x[3][w] << 16)};
-        const u32x2 odd = {(x[0][w] >> 16) | (x[1][w] & 0xffff0000u),
-                           (x[2][w] >> 16) | (x[3][w] & 0xffff0000u)};
-        *(u32x2*)(vt_lds + (8 * dc + 2 * w) * VP + 4 * kq) = even;
-        *(u32x2*)(vt_lds + (8 * dc + 2 * w + 1) * VP + 4 * kq) = odd;
-      }
-    }
-    __syncthreads();
-
     // Under causal masking a wave whose rows all precede the tile's first key
-    // has nothing to do for this tile (it still joins the barriers above).
-    if (CAUSAL && key0 > wave_row0 + T::kRowsPerWave - 1) continue;
+    // has nothing to do for it (it still joins the loads and barriers).
+    if (CAUSAL && key0 > wave_row0 + SH::kRowsPerWave - 1) continue;
 
-    // S^T = K_j Q^T: NKB blocks of 32 keys x 32 rows.
-    f32x16 acc_s[NKB];
+    const int stage = j % NS;
+    const unsigned char* v_lds = smem + stage * 2 * TB + TB;
+
+    // S^T = K_j Q^T. Chunk (2 s + hi) ^ (l32 & 7) of a key row is byte
+    // offset (32 s) ^ (16 (hi ^ (l32 & 7))) within it, and row and stage
+    // bases are multiples of 256 bytes, so the address of k-step s is one
+    // per-tile base XOR 32 s.
+    f32x16 acc_s[RB][NKB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) acc_s[rb][kb] = f32x16{};
+    const uint32_t k_base = (uint32_t)(stage * 2 * TB) + k_lane;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      acc_s[kb] = f32x16{};
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
-        const u32x4 a = *(const u32x4*)(k_lds + (32 * kb + l32) * KP + 16 * s + 8 * hi);
-        acc_s[kb] = E::mfma(a, qf[s], acc_s[kb]);
+        const uint32_t off = (k_base ^ (uint32_t)(32 * s)) + (uint32_t)(kb * 32 * CPR * 16);
+        const u32x4 a = *(const u32x4*)(smem + off);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc_s[rb][kb] = E::mfma(a, qf[rb][s], acc_s[rb][kb]);
       }
     }
 
-    // Mask keys >= S (ragged tail) and, under causal masking, keys > row.
-    // Masked tiles are scaled first and masked in the scaled (base-2)
-    // domain, so a zero scale never meets a -inf score; c_eff is then 1.
-    float c_eff = c;
-    const bool need_mask =
-        (key0 + Bc > S) || (CAUSAL && key0 + Bc - 1 > wave_row0);
-    if (need_mask) {
+    // Online softmax, one row per lane and row block.
+    float c_eff[RB], tmax[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = wave_row0 + 32 * rb + l32;
+      c_eff[rb] = c;
+      // Mask keys >= S (ragged tail) and, under causal masking, keys > row.
+      // Masked tiles are scaled first and masked in the scaled domain, so a
+      // zero scale never meets a -inf score; c_eff is then 1.
+      const bool need_mask =
+          (key0 + Bc > S) || (CAUSAL && key0 + Bc - 1 > wave_row0 + 32 * rb);
+      if (need_mask) {
+        // register r of key block kb holds key key0 + 32 kb + 8 (r / 4) + 4 hi
+        // + r % 4; it is kept iff that offset from key0 + 4 hi is < lim
+        const int base_key = key0 + 4 * hi;
+        const int lim = CAUSAL ? min(S - base_key, row - base_key + 1) : S - base_key;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = 32 * kb + 8 * (r / 4) + (r % 4);
+            acc_s[rb][kb][r] = rel < lim ? acc_s[rb][kb][r] * c : -INFINITY;
+          }
+        c_eff[rb] = 1.f;
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kb + 8 * (r / 4) + 4 * hi + (r % 4);
-          const bool masked = key >= S || (CAUSAL && key > row);
-          acc_s[kb][r] = masked ? -INFINITY : acc_s[kb][r] * c;
-        }
-      c_eff = 1.f;
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc_s[rb][kb][r]), acc_s[rb][kb][r + 1]);
+      tmax[rb] = xor32_max(mx) * c_eff[rb];
     }
 
-    // Online softmax for this lane's row.
-    float mx = -INFINITY;
+    // Lazy rescale: raise the reference max only when a row's tile max
+    // exceeds it by more than kTau (always on a row's first tile).
+    bool need = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int rb = 0; rb < RB; ++rb) need |= tmax[rb] > m_run[rb] + kTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb][r]);
-    mx = max_with_other_half(mx);
-    const float m_new = fmaxf(m_run, mx * c_eff);
-    // A row with no unmasked key so far keeps m = -inf; use 0 as its
-    // exponent reference so that no -inf - (-inf) is formed.
-    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    l_run *= alpha;
+      for (int rb = 0; rb < RB; ++rb) {
+        const float m_new = tmax[rb] > m_run[rb] + kTau ? tmax[rb] : m_run[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+        l_rnd[rb] *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-
-    uint32_t pk[NKB][8];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][r], c_eff, -m_ref));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][r + 1], c_eff, -m_ref));
-        l_run += p0 + p1;
-        pk[kb][r / 2] = E::pack2(p0, p1);
+        for (int db = 0; db < NDB; ++db) acc_o[rb][db] *= alpha;
+        m_run[rb] = m_new;
       }
+    }
 
-    // O^T += V_j^T P^T. B operand element e of step (kb, h) is accumulator
-    // register 8h + e, i.e. key 32 kb + 16 h + 8 (e / 4) + 4 hi + e % 4;
-    // the A operand gathers V^T at the same keys.
+    // P = 2^(t - m), rounded to the input dtype for the P V product.
+    u32x4 pb[RB][NKB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      // a row with no unmasked key so far keeps m = -inf; use 0 as its
+      // exponent reference so that no -inf - (-inf) is formed
+      const float m_ref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int r = 8 * h + 2 * w;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[rb][kb][r], c_eff[rb], -m_ref));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[rb][kb][r + 1], c_eff[rb], -m_ref));
+            const uint32_t pk = E::pack2(p0, p1);
+            l_run[rb] += p0 + p1;
+            l_rnd[rb] = E::add_pair(pk, l_rnd[rb]);
+            pb[rb][kb][h][w] = pk;
+          }
+    }
+
+    // O^T += V_j^T P^T.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4 b = {pk[kb][4 * h], pk[kb][4 * h + 1], pk[kb][4 * h + 2], pk[kb][4 * h + 3]};
+        const unsigned char* vrow = v_lds + (32 * kb + 16 * h) * CPR * 16;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const uint16_t* base = vt_lds + (32 * db + l32) * VP + 32 * kb + 16 * h + 4 * hi;
-          const u32x2 a0 = *(const u32x2*)base;
-          const u32x2 a1 = *(const u32x2*)(base + 8);
-          const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-          acc_o[db] = E::mfma(a, b, acc_o[db]);
+          const unsigned char* vp = vrow + (db & 1 ? vt_odd : vt_even) + db * 4 * 16;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+          const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * CPR * 16));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+          const u32x4 a = {lo2[0], lo2[1], up2[0], up2[1]};
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = E::mfma(a, pb[rb][kb][h], acc_o[rb][db]);
         }
       }
-    m_run = m_new;
   }
 
-  // Epilogue: O = O~ / l, rounded once to the input dtype; lse = ln2 (m + log2 l).
-  const float l_tot = sum_with_other_half(l_run);
-  if (row < S) {
-    const float inv = 1.0f / l_tot;
+  // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, which
+  // makes O an exact convex combination of V rows; lse = ln2 (m + log2 l)
+  // from the unrounded sum.
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = wave_row0 + 32 * rb + l32;
+    const float l_tot = xor32_sum(l_run[rb]);
+    const float l_o = xor32_sum(l_rnd[rb]);
+    if (row < S) {
+      const float inv = 1.0f / l_o;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 out = {E::pack2(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
-                           E::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
-        *(u32x2*)(o + head + (size_t)row * D + 32 * db + 8 * g + 4 * hi) = out;
-      }
-    if (hi == 0) lse[(size_t)bh * S + row] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 out = {E::pack2(acc_o[rb][db][4 * g] * inv, acc_o[rb][db][4 * g + 1] * inv),
+                             E::pack2(acc_o[rb][db][4 * g + 2] * inv, acc_o[rb][db][4 * g + 3] * inv)};
+          *(u32x2*)(o + head + (size_t)row * D + 32 * db + 8 * g + 4 * hi) = out;
+        }
+      if (hi == 0) lse[(size_t)bh * S + row] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
   }
 }
 
 template <int D, int DT, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int S, float scale, hipStream_t stream) {
-  using T = Tile<D>;
-  const dim3 grid((unsigned)((S + T::kBr - 1) / T::kBr), (unsigned)H, (unsigned)B);
-  const dim3 block(T::kThreads);
+  using SH = Shape<D>;
+  const dim3 grid((unsigned)((S + SH::kBr - 1) / SH::kBr), (unsigned)H, (unsigned)B);
+  const dim3 block(SH::kThreads);
   fa2_fwd_kernel<D, DT, CAUSAL><<<grid, block, 0, stream>>>(
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
       scale * kLog2e);
@@ -354,9 +534,9 @@ extern "C" int fa2_supported(int D, int dtype) {
 
 extern "C" int fa2_rows_per_workgroup(int D) {
   switch (D) {
-    case 64: return Tile<64>::kBr;
-    case 128: return Tile<128>::kBr;
-    case 256: return Tile<256>::kBr;
+    case 64: return Shape<64>::kBr;
+    case 128: return Shape<128>::kBr;
+    case 256: return Shape<256>::kBr;
     default: return 0;
   }
 }
@@ -365,7 +545,9 @@ extern "C" const char* fa2_status_string(int status) {
   switch (status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
-    case FA2_ERR_SHAPE: return "B, H and S must be >= 1, B and H <= 65535, and B*H*S*D must fit in int64";
+    case FA2_ERR_SHAPE:
+      return "B, H and S must be >= 1, B and H <= 65535, one head (S*D elements) under 2 GiB, "
+             "and the grid within 2^31 workgroups";
     case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA2_ERR_DTYPE: return "dtype must be FA2_F16 or FA2_BF16";
     case FA2_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";
@@ -383,13 +565,15 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, flo
   if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535) return FA2_ERR_SHAPE;
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
   if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
-  // B, H <= 65535, S < 2^31, D <= 256: B*H*S*D < 2^71 can overflow int64.
-  const unsigned __int128 elems = (unsigned __int128)B * H * S * D;
-  if (elems > (unsigned __int128)(INT64_MAX / 2)) return FA2_ERR_SHAPE;
+  // One head, plus one tile of keys past its end, is addressed with 32-bit
+  // byte offsets (buffer loads): keep it under 2 GiB.
+  if (((long long)S + 256) * D * 2 > (long long)INT32_MAX) return FA2_ERR_SHAPE;
+  const unsigned long long elems =
+      (unsigned long long)B * (unsigned long long)H * (unsigned long long)S * (unsigned long long)D;
   // the kernel linearises its block index in a 32-bit int
-  const unsigned long long blocks =
-      (unsigned long long)(((long long)S + fa2_rows_per_workgroup(D) - 1) / fa2_rows_per_workgroup(D)) *
-      (unsigned long long)H * (unsigned long long)B;
+  const int rows = fa2_rows_per_workgroup(D);
+  const unsigned long long blocks = (((unsigned long long)S + rows - 1) / rows) *
+                                    (unsigned long long)H * (unsigned long long)B;
   if (blocks > (unsigned long long)INT32_MAX) return FA2_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
