@@ -61,6 +61,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <type_traits>
 #include <cstdint>
 #include <cstring>
 
@@ -123,41 +124,55 @@ template <> struct Elem<FA2_BF16> {
 };
 
 // Tile shape per head dimension.
-//   kRowBlocks  32-row MFMA blocks per wave (each K/V fragment read from LDS
-//               feeds kRowBlocks MFMAs, so more blocks mean fewer LDS bytes
-//               per FLOP, at the cost of registers)
-//   kBc         keys per tile;  kStages  LDS ring depth
+//   kWaves      waves per workgroup (they share the LDS rings)
+//   kRowBlocks  32-row MFMA blocks per wave
+//   kBc         keys per tile
 //   kWavesPerSimd  waves per SIMD the register budget is sized for
+// K and V each have a two-stage LDS ring: iteration j reads K of tile j + 1
+// and V of tile j while K of tile j + 2 and V of tile j + 1 load.
 template <int D> struct Tile;
 template <> struct Tile<64> {
-  static constexpr int kRowBlocks = 2, kBc = 64, kStages = 3, kWavesPerSimd = 1;
+  static constexpr int kWaves = 4, kRowBlocks = 1, kBc = 64, kWavesPerSimd = 2;
 };
 template <> struct Tile<128> {
-  static constexpr int kRowBlocks = 2, kBc = 32, kStages = 4, kWavesPerSimd = 2;
+  static constexpr int kWaves = 4, kRowBlocks = 1, kBc = 64, kWavesPerSimd = 2;
 };
 template <> struct Tile<256> {
-  static constexpr int kRowBlocks = 1, kBc = 64, kStages = 2, kWavesPerSimd = 1;
+  static constexpr int kWaves = 4, kRowBlocks = 1, kBc = 32, kWavesPerSimd = 1;
 };
 
 template <int D> struct Shape {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = Tile<D>::kWaves;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kRB = Tile<D>::kRowBlocks;
   static constexpr int kRowsPerWave = 32 * kRB;
   static constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
   static constexpr int kBc = Tile<D>::kBc;
-  static constexpr int kStages = Tile<D>::kStages;
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per key row
   static constexpr int kTileBytes = kBc * D * 2;     // one K or one V tile
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per K (or V) tile
-  static constexpr int kLdsBytes = kStages * 2 * kTileBytes;
+  static constexpr int kLdsBytes = 4 * kTileBytes;   // K ring (2) + V ring (2)
   static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-// Chunk swizzles (XOR on the 16-byte chunk index within a key row).
-__device__ __forceinline__ int swz_k(int row) { return row & 7; }
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+// Chunk swizzles (XOR on the 16-byte chunk index within a key row). gfx950
+// LDS has 64 banks (256 bytes per cycle); a ds_read_b128 serves 16 lanes per
+// cycle and a ds_read_b64_tr_b16 32 lanes, so:
+//   K: 16 lanes read chunk c of 16 consecutive rows -> XOR row & 15 puts
+//      them in 16 distinct 16-byte bank groups (D = 64: two rows share a
+//      256-byte line, so XOR (row / 2) & 7 instead);
+//   V: 32 lanes read chunks 4 db .. 4 db + 3 of 4 consecutive rows -> XOR
+//      4 (row & 3) spreads them over all 16 groups (D = 64: XOR
+//      4 ((row / 2) & 1), rows r and r + 1 already sit in different halves).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 64 ? (row >> 1) & 7 : row & 15;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 64 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
+}
 
 // s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding; expcnt not waited).
 template <int N>
@@ -166,19 +181,8 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-// Wait until at most PER * n vector-memory loads are outstanding, n <= MAXN
-// known only at run time (s_waitcnt takes an immediate).
-template <int PER, int MAXN>
-__device__ __forceinline__ void wait_for_tile(int n) {
-  if constexpr (MAXN <= 0) {
-    wait_vm_lgkm0<0>();
-  } else {
-    if (n >= MAXN)
-      wait_vm_lgkm0<PER * MAXN>();
-    else
-      wait_for_tile<PER, MAXN - 1>(n);
-  }
-}
+// x made wave-uniform (scalar register); x must already be equal in all lanes.
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ void workgroup_barrier() {
   __asm__ volatile("s_barrier" ::: "memory");
@@ -195,33 +199,270 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Start the loads of one K tile and one V tile into LDS stage `st`: this
-// wave's LPW 1 KiB blocks of each, from byte `base` of the head (tile t
-// starts at t * TB since a tile is Bc whole key rows). LDS slot
-// p = block * 64 + lane receives chunk (p % CPR) ^ swz(row) of key row p / CPR.
-template <int D, int LPW, int TB>
-__device__ __forceinline__ void issue_tile(unsigned char* smem, int wave, int lane,
-                                           __amdgpu_buffer_rsrc_t k_rsrc,
-                                           __amdgpu_buffer_rsrc_t v_rsrc, uint32_t base,
-                                           int st) {
+// Per-lane byte offsets, within one tile, of the 16-byte chunks this wave
+// loads: LDS slot p = block * 64 + lane of the tile receives chunk
+// (p % CPR) ^ swz(row) of key row p / CPR.
+template <int D, int LPW, bool IS_V>
+__device__ __forceinline__ void tile_load_offsets(int wave, int lane, uint32_t (&off)[LPW]) {
   constexpr int CPR = D / 8;
-  unsigned char* kst = smem + st * 2 * TB;
-  unsigned char* vst = kst + TB;
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int p = (wave * LPW + i) * 64 + lane;
     const int r = p / CPR, cp = p % CPR;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (lds_void*)(kst + (wave * LPW + i) * 1024),
-                                             16, base + (uint32_t)((r * D + (cp ^ swz_k(r)) * 8) * 2),
-                                             0, 0, 0);
+    const int c = cp ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+    off[i] = (uint32_t)((r * D + c * 8) * 2);
   }
+}
+
+// Start loading tile t of a head (K or V) into LDS at `dst`: this wave's LPW
+// 1 KiB blocks. The buffer is rebased on the tile, so its record count ends
+// at the end of the head and loads past S return zero.
+template <int LPW, int TB>
+__device__ __forceinline__ void load_tile(const unsigned char* head_base, uint32_t head_bytes,
+                                          int t, unsigned char* dst, int wave,
+                                          const uint32_t* off) {
+  // both values are wave-uniform; readfirstlane keeps them (and so the buffer
+  // descriptor) in scalar registers
+  const uint32_t start = (uint32_t)t * TB;
+  const uint32_t left =
+      (uint32_t)wave_uniform((int)(head_bytes - (start < head_bytes ? start : head_bytes)));
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + start), 0, (int)left, kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int p = (wave * LPW + i) * 64 + lane;
-    const int r = p / CPR, cp = p % CPR;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (lds_void*)(vst + (wave * LPW + i) * 1024),
-                                             16, base + (uint32_t)((r * D + (cp ^ swz_v(r)) * 8) * 2),
-                                             0, 0, 0);
+  for (int i = 0; i < LPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * LPW + i) * 1024), 16,
+                                             off[i], 0, 0, 0);
+}
+
+// S^T = K_t Q^T for one tile whose K sits at byte k_stage of LDS. Chunk
+// (2 s + hi) ^ x of a key row (x = swz_k(row)) is byte offset
+// (32 s) ^ (16 (hi ^ x)) within it, and row and stage bases have no bits in
+// common with it, so the address of k-step s is one per-tile base XOR 32 s.
+template <int D, int DT, int RB, int NKB>
+__device__ __forceinline__ void tile_scores(const unsigned char* smem, uint32_t k_stage, uint32_t k_lane,
+                                            const u32x4 (&qf)[RB][D / 16],
+                                            f32x16 (&acc)[RB][NKB]) {
+  constexpr int CPR = D / 8, NDS = D / 16;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = f32x16{};
+  const uint32_t k_base = k_stage + k_lane;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      const uint32_t off = (k_base ^ (uint32_t)(32 * s)) + (uint32_t)(kb * 32 * CPR * 16);
+      const u32x4 a = *(const u32x4*)(smem + off);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = Elem<DT>::mfma(a, qf[rb][s], acc[rb][kb]);
+    }
+}
+
+// Mask one tile's scores. Register r of key block kb holds key
+// key0 + 32 kb + 8 (r / 4) + 4 hi + r % 4; it is kept iff that key is < S
+// and (causal) <= row. Masked tiles are scaled here and masked in the scaled
+// domain, so a zero scale never meets a -inf score; their c_eff is then 1,
+// else c.
+template <int RB, int NKB, bool CAUSAL>
+__device__ __forceinline__ void tile_mask(f32x16 (&acc)[RB][NKB], int key0, int row0, int S,
+                                          float c, int l32, int hi, float (&c_eff)[RB]) {
+  constexpr int Bc = 32 * NKB;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    c_eff[rb] = c;
+    const int row = row0 + 32 * rb + l32;
+    if ((key0 + Bc > S) || (CAUSAL && key0 + Bc - 1 > row0 + 32 * rb)) {
+      const int base_key = key0 + 4 * hi;
+      const int lim = CAUSAL ? min(S - base_key, row - base_key + 1) : S - base_key;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = 32 * kb + 8 * (r / 4) + (r % 4);
+          acc[rb][kb][r] = rel < lim ? acc[rb][kb][r] * c : -INFINITY;
+        }
+      c_eff[rb] = 1.f;
+    }
+  }
+}
+
+// Whether any row block of the wave needs masking for the tile at key0.
+template <int RB, int NKB, bool CAUSAL>
+__device__ __forceinline__ bool tile_needs_mask(int key0, int row0, int S) {
+  constexpr int Bc = 32 * NKB;
+  return (key0 + Bc > S) || (CAUSAL && key0 + Bc - 1 > row0);
+}
+
+// Each row's tile max of t = c_eff * (masked) scores.
+template <int RB, int NKB>
+__device__ __forceinline__ void tile_max(const f32x16 (&acc)[RB][NKB], const float (&c_eff)[RB],
+                                         float (&tmax)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[rb][kb][r]), acc[rb][kb][r + 1]);
+    tmax[rb] = xor32_max(mx) * c_eff[rb];
+  }
+}
+
+// Lazy rescale: raise a row's reference max only when its tile max exceeds
+// it by more than kTau (always on the row's first tile, where m = -inf).
+template <int RB, int NDB>
+__device__ __forceinline__ void maybe_rescale(const float (&tmax)[RB], float (&m_run)[RB],
+                                              float (&l_run)[RB], float (&l_rnd)[RB],
+                                              f32x16 (&acc_o)[RB][NDB]) {
+  bool need = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) need |= tmax[rb] > m_run[rb] + kTau;
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float m_new = tmax[rb] > m_run[rb] + kTau ? tmax[rb] : m_run[rb];
+      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+      l_run[rb] *= alpha;
+      l_rnd[rb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[rb][db] *= alpha;
+      m_run[rb] = m_new;
+    }
+  }
+}
+
+// P = 2^(t - m) rounded to the input dtype, packed as the B operand of the
+// P V product; l_run sums P as computed (for lse), l_rnd as rounded (for O).
+template <int DT, int RB, int NKB>
+__device__ __forceinline__ void tile_probs(const f32x16 (&acc)[RB][NKB], const float (&c_eff)[RB],
+                                           const float (&m_run)[RB], float (&l_run)[RB],
+                                           float (&l_rnd)[RB], u32x4 (&pb)[RB][NKB][2]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // a row with no unmasked key so far keeps m = -inf; use 0 as its
+    // exponent reference so that no -inf - (-inf) is formed
+    const float m_ref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r = 8 * h + 2 * w;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r], c_eff[rb], -m_ref));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r + 1], c_eff[rb], -m_ref));
+          const uint32_t pk = Elem<DT>::pack2(p0, p1);
+          l_run[rb] += p0 + p1;
+          l_rnd[rb] = Elem<DT>::add_pair(pk, l_rnd[rb]);
+          pb[rb][kb][h][w] = pk;
+        }
+  }
+}
+
+// The main block of one pipeline step, written in the order it should
+// issue (two waves per SIMD fill each other's gaps; the source order gives
+// the scheduler the interleave):
+//   phase 1, one step per 16-wide k-step of the scores of tile j + 1: the RB
+//     matrix ops of that k-step (its K operand read PFK steps ahead) beside
+//     the next PPS probability pairs of tile j on the vector unit;
+//   phase 2, one step per (key block, half, head-dim block) of the P V
+//     product of tile j: its RB matrix ops (V^T operands read PFV steps
+//     ahead) beside a slice of tile j + 1's row max.
+// Probability pairs come in the order the P V steps consume them.
+template <int D, int DT, int RB, int NKB>
+__device__ __forceinline__ void pipeline_block(
+    const unsigned char* smem, uint32_t k_stage, uint32_t v_stage, uint32_t k_lane, uint32_t vt_x,
+    const u32x4 (&qf)[RB][D / 16], const f32x16 (&cur)[RB][NKB], const float (&ce_cur)[RB],
+    const float (&m_run)[RB], float (&l_run)[RB], float (&l_rnd)[RB], f32x16 (&nxt)[RB][NKB],
+    float (&mx_nxt)[RB], f32x16 (&acc_o)[RB][D / 32]) {
+  using E = Elem<DT>;
+  constexpr int CPR = D / 8, NDS = D / 16, NDB = D / 32;
+  constexpr int NS1 = NKB * NDS;                   // phase-1 steps
+  constexpr int NPAIR = RB * NKB * 8;              // probability pairs per lane
+  constexpr int PPS = (NPAIR + NS1 - 1) / NS1;     // pairs per phase-1 step
+  constexpr int NS2 = NKB * 2 * NDB;               // phase-2 steps
+  constexpr int NMAX = RB * NKB * 8;               // max3 folds of tile j + 1
+  constexpr int MPS = (NMAX + NS2 - 1) / NS2;      // folds per phase-2 step
+  constexpr int PFK = 3, PFV = 2;                  // operand read-ahead (steps)
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) nxt[rb][kb] = f32x16{};
+  float m_ref[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    // a row with no unmasked key so far keeps m = -inf; use 0 as its
+    // exponent reference so that no -inf - (-inf) is formed
+    m_ref[rb] = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+    mx_nxt[rb] = -INFINITY;
+  }
+
+  // phase 1
+  const uint32_t k_base = k_stage + k_lane;
+  auto k_read = [&](int st) {
+    const int kb = st / NDS, s = st % NDS;
+    const uint32_t off = (k_base ^ (uint32_t)(32 * s)) + (uint32_t)(kb * 32 * CPR * 16);
+    return *(const u32x4*)(smem + off);
+  };
+  u32x4 kq[PFK];
+#pragma unroll
+  for (int i = 0; i < PFK; ++i)
+    if (i < NS1) kq[i] = k_read(i);
+  u32x4 pb[RB][NKB][2];
+#pragma unroll
+  for (int st = 0; st < NS1; ++st) {
+    const int kb = st / NDS, s = st % NDS;
+    const u32x4 a = kq[st % PFK];
+    if (st + PFK < NS1) kq[st % PFK] = k_read(st + PFK);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) nxt[rb][kb] = E::mfma(a, qf[rb][s], nxt[rb][kb]);
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+      const int p = st * PPS + pp;  // pair p = ((kb * 2 + h) * RB + rb) * 4 + w
+      if (p < NPAIR) {
+        const int w = p % 4, rb = (p / 4) % RB, h = (p / (4 * RB)) % 2, pkb = p / (8 * RB);
+        const int r = 8 * h + 2 * w;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[rb][pkb][r], ce_cur[rb], -m_ref[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[rb][pkb][r + 1], ce_cur[rb], -m_ref[rb]));
+        const uint32_t pk = E::pack2(p0, p1);
+        l_run[rb] += p0 + p1;
+        l_rnd[rb] = E::add_pair(pk, l_rnd[rb]);
+        pb[rb][pkb][h][w] = pk;
+      }
+    }
+  }
+
+  // phase 2
+  const unsigned char* v_lds = smem + v_stage;
+  auto v_read = [&](int st) {
+    const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
+    const unsigned char* vp = v_lds + (32 * kb + 16 * h) * CPR * 16 + (vt_x ^ (uint32_t)(64 * db));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * CPR * 16));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+    return u32x4{lo2[0], lo2[1], up2[0], up2[1]};
+  };
+  u32x4 vq[PFV];
+#pragma unroll
+  for (int i = 0; i < PFV; ++i)
+    if (i < NS2) vq[i] = v_read(i);
+#pragma unroll
+  for (int st = 0; st < NS2; ++st) {
+    const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
+    const u32x4 a = vq[st % PFV];
+    if (st + PFV < NS2) vq[st % PFV] = v_read(st + PFV);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = E::mfma(a, pb[rb][kb][h], acc_o[rb][db]);
+#pragma unroll
+    for (int mm = 0; mm < MPS; ++mm) {
+      const int f = st * MPS + mm;  // fold f = (rb * NKB + kb) * 8 + i
+      if (f < NMAX) {
+        const int i = f % 8, fkb = (f / 8) % NKB, rb = f / (8 * NKB);
+        mx_nxt[rb] = fmaxf(fmaxf(mx_nxt[rb], nxt[rb][fkb][2 * i]), nxt[rb][fkb][2 * i + 1]);
+      }
+    }
   }
 }
 
@@ -232,16 +473,19 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
     int S, float c /* scale * log2(e) */) {
   using SH = Shape<D>;
   using E = Elem<DT>;
-  constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr, NS = SH::kStages;
+  constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
   constexpr int CPR = SH::kChunksPerRow, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
   constexpr int NKB = Bc / 32;  // 32-key blocks per tile
   constexpr int NDS = D / 16;   // k-steps of 16 over the head dim (S^T product)
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O^T
 
+  // K ring (stages 0, 1) then V ring (stages 0, 1), TB bytes each.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SH::kLdsBytes];
+  constexpr uint32_t kK0 = 0, kK1 = TB, kV0 = 2 * TB, kV1 = 3 * TB;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = wave_uniform(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Workgroup -> (query tile, batch*head). Tiles are taken in descending
@@ -269,27 +513,27 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
     }
   }
 
-  // K and V of this head as bounds-checked byte buffers.
+  // K and V of this head, loaded through bounds-checked buffers.
   const uint32_t head_bytes = (uint32_t)S * D * 2;
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(k + head), 0, (int)head_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(v + head), 0, (int)head_bytes, kBufferFlags);
+  const unsigned char* k_head = (const unsigned char*)(k + head);
+  const unsigned char* v_head = (const unsigned char*)(v + head);
+  uint32_t k_off[LPW], v_off[LPW];
+  tile_load_offsets<D, LPW, false>(wave, lane, k_off);
+  tile_load_offsets<D, LPW, true>(wave, lane, v_off);
 
   // LDS read offsets that do not depend on the tile.
-  // K^T operand: row 32 kb + l32, chunk (2 s + hi) ^ (l32 & 7).
-  const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ (l32 & 7)));
+  // K^T operand: row 32 kb + l32, chunk (2 s + hi) ^ swz_k(l32).
+  const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ swz_k<D>(l32)));
   // V^T operand: row 32 kb + 16 h + 4 hi + (lane % 16) / 4 (+8 for e >= 4),
   // dims 32 db + 16 ((lane / 16) % 2) + 4 (lane % 4) .. +3, i.e. chunk
-  // 4 db + vt_chunk, byte 8 (lane % 2) within it. The swizzle XORs bits 1-2
-  // of the chunk index; bit 2 is bit 0 of db, so even and odd db blocks get
-  // their own base: chunk (4 db + c) ^ w = 4 (db ^ (w >> 2)) + (c ^ (w & 3)).
+  // 4 db + vt_chunk, byte 8 (lane % 2) within it. The swizzle is 4 w for a
+  // per-row w, and (4 db + c) ^ 4 w = 4 (db ^ w) + c, so head-dim block db
+  // is at vt_x ^ (64 db) with vt_x = the db = 0 offset plus 64 w (the bits
+  // of 64 db are clear in every other term).
   const int vt_row = 4 * hi + (lane & 15) / 4;
   const int vt_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int vt_w = swz_v(vt_row);
-  const int vt_common = (vt_row * CPR + (vt_chunk ^ (vt_w & 3))) * 16 + 8 * (lane & 1);
-  const int vt_even = vt_common + 64 * (vt_w >> 2);  // db even: 4 (db ^ b) = 4 db + 4 b
-  const int vt_odd = vt_common - 64 * (vt_w >> 2);   // db odd:  4 (db ^ b) = 4 db - 4 b
+  const uint32_t vt_x = (uint32_t)((vt_row * CPR + vt_chunk) * 16 + 8 * (lane & 1) +
+                                   64 * (swz_v<D>(vt_row) >> 2));
 
   f32x16 acc_o[RB][NDB];
 #pragma unroll
@@ -308,143 +552,76 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
   }
 
   const int kv_end = CAUSAL ? min(q0 + Br, S) : S;
-  const int n_tiles = (kv_end + Bc - 1) / Bc;
+  const int n_tiles = (kv_end + Bc - 1) / Bc;  // tiles the workgroup loads
+  // tiles this wave computes (under causal masking the later tiles of the
+  // workgroup lie wholly above this wave's rows)
+  const int n_act =
+      CAUSAL ? min(n_tiles, (wave_row0 + SH::kRowsPerWave + Bc - 1) / Bc) : n_tiles;
 
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < n_tiles) issue_tile<D, LPW, TB>(smem, wave, lane, k_rsrc, v_rsrc, (uint32_t)t * TB, t);
+  // Software pipeline. Iteration j computes the scores of tile j + 1 on the
+  // matrix cores while the vector unit turns tile j's scores into P, then the
+  // P V product of tile j while the vector unit takes tile j + 1's row max.
+  // At its top every load issued in iteration j - 1 (K of tile j + 1, V of
+  // tile j) has landed, and after the barrier every wave is done with
+  // iteration j - 1, so K of tile j + 2 goes into tile j's K stage and V of
+  // tile j + 1 into tile j - 1's V stage.
+  load_tile<LPW, TB>(k_head, head_bytes, 0, smem + kK0, wave, k_off);
+  load_tile<LPW, TB>(v_head, head_bytes, 0, smem + kV0, wave, v_off);
+  if (n_tiles > 1) load_tile<LPW, TB>(k_head, head_bytes, 1, smem + kK1, wave, k_off);
 
-  for (int j = 0; j < n_tiles; ++j) {
-    // This wave's loads of tile j are done (those of the tiles after it that
-    // are already issued may still be in flight); after the barrier every
-    // wave's are, and every wave has finished reading tile j - 1, whose stage
-    // is refilled next.
-    wait_for_tile<2 * LPW, NS - 2>(min(NS - 2, n_tiles - 1 - j));
+  f32x16 s_a[RB][NKB], s_b[RB][NKB];
+  float ce_a[RB], ce_b[RB];
+  wait_vm_lgkm0<0>();
+  workgroup_barrier();
+  if (n_act > 0) {
+    float tm[RB];
+    tile_scores<D, DT, RB, NKB>(smem, kK0, k_lane, qf, s_a);
+    tile_mask<RB, NKB, CAUSAL>(s_a, 0, wave_row0, S, c, l32, hi, ce_a);
+    tile_max<RB, NKB>(s_a, ce_a, tm);
+    maybe_rescale<RB, NDB>(tm, m_run, l_run, l_rnd, acc_o);
+  }
+
+  // One pipeline step for tile j with parity PAR = j % 2 (known at compile
+  // time after unrolling by two); `cur` holds tile j's scores, `nxt` receives
+  // tile j + 1's.
+  auto step = [&](auto par, int j, f32x16 (&cur)[RB][NKB], float (&ce_cur)[RB],
+                  f32x16 (&nxt)[RB][NKB], float (&ce_nxt)[RB]) {
+    constexpr int PAR = decltype(par)::value;
+    constexpr uint32_t k_next = PAR ? kK0 : kK1;  // K of tile j + 1
+    constexpr uint32_t k_free = PAR ? kK1 : kK0;  // K of tile j (done)
+    constexpr uint32_t v_cur = PAR ? kV1 : kV0;   // V of tile j
+    constexpr uint32_t v_free = PAR ? kV0 : kV1;  // V of tile j - 1 (done)
+    wait_vm_lgkm0<0>();
     workgroup_barrier();
-    if (j + NS - 1 < n_tiles)
-      issue_tile<D, LPW, TB>(smem, wave, lane, k_rsrc, v_rsrc, (uint32_t)(j + NS - 1) * TB,
-                             (j + NS - 1) % NS);
-
-    const int key0 = j * Bc;
-    // Under causal masking a wave whose rows all precede the tile's first key
-    // has nothing to do for it (it still joins the loads and barriers).
-    if (CAUSAL && key0 > wave_row0 + SH::kRowsPerWave - 1) continue;
-
-    const int stage = j % NS;
-    const unsigned char* v_lds = smem + stage * 2 * TB + TB;
-
-    // S^T = K_j Q^T. Chunk (2 s + hi) ^ (l32 & 7) of a key row is byte
-    // offset (32 s) ^ (16 (hi ^ (l32 & 7))) within it, and row and stage
-    // bases are multiples of 256 bytes, so the address of k-step s is one
-    // per-tile base XOR 32 s.
-    f32x16 acc_s[RB][NKB];
+    if (j + 2 < n_tiles) load_tile<LPW, TB>(k_head, head_bytes, j + 2, smem + k_free, wave, k_off);
+    if (j + 1 < n_tiles) load_tile<LPW, TB>(v_head, head_bytes, j + 1, smem + v_free, wave, v_off);
+    if (j < n_act) {
+      // scores of tile j + 1 || probabilities of tile j, then P V of tile j ||
+      // row max of tile j + 1 (past the wave's last tile the scores come from a
+      // stale stage and are never used)
+      float mx[RB];
+      pipeline_block<D, DT, RB, NKB>(smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run,
+                                     l_run, l_rnd, nxt, mx, acc_o);
+      if (j + 1 < n_act) {
+        float tm[RB];
+        if (tile_needs_mask<RB, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S)) {
+          // boundary tile: mask, then take the max again
+          tile_mask<RB, NKB, CAUSAL>(nxt, (j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
+          tile_max<RB, NKB>(nxt, ce_nxt, tm);
+        } else {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) acc_s[rb][kb] = f32x16{};
-    const uint32_t k_base = (uint32_t)(stage * 2 * TB) + k_lane;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int s = 0; s < NDS; ++s) {
-        const uint32_t off = (k_base ^ (uint32_t)(32 * s)) + (uint32_t)(kb * 32 * CPR * 16);
-        const u32x4 a = *(const u32x4*)(smem + off);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc_s[rb][kb] = E::mfma(a, qf[rb][s], acc_s[rb][kb]);
-      }
-    }
-
-    // Online softmax, one row per lane and row block.
-    float c_eff[RB], tmax[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int row = wave_row0 + 32 * rb + l32;
-      c_eff[rb] = c;
-      // Mask keys >= S (ragged tail) and, under causal masking, keys > row.
-      // Masked tiles are scaled first and masked in the scaled domain, so a
-      // zero scale never meets a -inf score; c_eff is then 1.
-      const bool need_mask =
-          (key0 + Bc > S) || (CAUSAL && key0 + Bc - 1 > wave_row0 + 32 * rb);
-      if (need_mask) {
-        // register r of key block kb holds key key0 + 32 kb + 8 (r / 4) + 4 hi
-        // + r % 4; it is kept iff that offset from key0 + 4 hi is < lim
-        const int base_key = key0 + 4 * hi;
-        const int lim = CAUSAL ? min(S - base_key, row - base_key + 1) : S - base_key;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rel = 32 * kb + 8 * (r / 4) + (r % 4);
-            acc_s[rb][kb][r] = rel < lim ? acc_s[rb][kb][r] * c : -INFINITY;
+          for (int rb = 0; rb < RB; ++rb) {
+            ce_nxt[rb] = c;
+            tm[rb] = xor32_max(mx[rb]) * c;
           }
-        c_eff[rb] = 1.f;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc_s[rb][kb][r]), acc_s[rb][kb][r + 1]);
-      tmax[rb] = xor32_max(mx) * c_eff[rb];
-    }
-
-    // Lazy rescale: raise the reference max only when a row's tile max
-    // exceeds it by more than kTau (always on a row's first tile).
-    bool need = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) need |= tmax[rb] > m_run[rb] + kTau;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float m_new = tmax[rb] > m_run[rb] + kTau ? tmax[rb] : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        l_run[rb] *= alpha;
-        l_rnd[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) acc_o[rb][db] *= alpha;
-        m_run[rb] = m_new;
-      }
-    }
-
-    // P = 2^(t - m), rounded to the input dtype for the P V product.
-    u32x4 pb[RB][NKB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // a row with no unmasked key so far keeps m = -inf; use 0 as its
-      // exponent reference so that no -inf - (-inf) is formed
-      const float m_ref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int r = 8 * h + 2 * w;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(acc_s[rb][kb][r], c_eff[rb], -m_ref));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(acc_s[rb][kb][r + 1], c_eff[rb], -m_ref));
-            const uint32_t pk = E::pack2(p0, p1);
-            l_run[rb] += p0 + p1;
-            l_rnd[rb] = E::add_pair(pk, l_rnd[rb]);
-            pb[rb][kb][h][w] = pk;
-          }
-    }
-
-    // O^T += V_j^T P^T.
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned char* vrow = v_lds + (32 * kb + 16 * h) * CPR * 16;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const unsigned char* vp = vrow + (db & 1 ? vt_odd : vt_even) + db * 4 * 16;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-          const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * CPR * 16));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
-          const u32x4 a = {lo2[0], lo2[1], up2[0], up2[1]};
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = E::mfma(a, pb[rb][kb][h], acc_o[rb][db]);
         }
+        maybe_rescale<RB, NDB>(tm, m_run, l_run, l_rnd, acc_o);
       }
+    }
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j, s_a, ce_a, s_b, ce_b);
+    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1, s_b, ce_b, s_a, ce_a);
   }
 
   // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, which
