@@ -20,13 +20,20 @@
 // and only the epilogue divides by l and writes lse = ln2 * (m + log2 l).
 // 2^(x log2 e) = e^x, so these are the pages' exp-based recurrences.
 //
-// The reference point m is the running row max, moved lazily: it is raised
-// (rescaling O~ and l by alpha = 2^(m_old - m_new), as the guide's
-// recurrence does) only when a tile's max exceeds it by more than kTau = 8.
-// Any m at or above the true running max minus kTau gives the same O and
-// lse exactly -- it cancels between O~ and l -- while P stays <= 2^8, far
-// inside fp16/bf16 range. l sums the *rounded* P that the P V product uses,
-// so O is an exact convex combination of V rows whatever the rounding of P.
+// The reference point m is set to the row max of the first key tile and
+// moved lazily after that: it is raised (rescaling O~ and l by
+// alpha = 2^(m_old - m_new), as the guide's recurrence does) only when one
+// lane's share of a tile's row sum of P exceeds kSumLimit = 2^12. Any m
+// gives the same O and lse in exact arithmetic -- it cancels between O~ and
+// l -- and every P of a tile that passes the test is at most 2^12, inside
+// the fp16/bf16 range, so the test replaces the per-tile row max of the
+// pages' recurrence on the vector unit. A tile that fails it is redone: its
+// row max is taken, m is raised to it, O~ and l are rescaled and its P is
+// recomputed. l sums P in fp32 as computed, before P is rounded for the
+// P V product, as the pages' l does, and gives lse; O is divided by a second
+// sum, of P as rounded, which makes it an exact convex combination of V rows
+// whatever the rounding of P (a near one-hot row then reproduces its V row
+// up to fp32 accumulation, not up to the rounding of its largest P).
 //
 // Matrix-core formulation. The wave computes the transposed products
 //   S^T = K_j Q^T   (A = K_j from LDS,   B = Q^T resident in registers)
@@ -83,7 +90,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
-constexpr float kTau = 8.0f;  // lazy-rescale threshold (base-2 units)
+constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile sum of P
 
 // Buffer resource word 3 for raw (unswizzled, stride 0) buffers on gfx9.
 constexpr int kBufferFlags = 0x00020000;
@@ -309,40 +316,35 @@ __device__ __forceinline__ void tile_max(const f32x16 (&acc)[RB][NKB], const flo
   }
 }
 
-// Lazy rescale: raise a row's reference max only when its tile max exceeds
-// it by more than kTau (always on the row's first tile, where m = -inf).
+// Raise each row's reference max to at least its tile max tmax, rescaling
+// O~ and both sums by alpha = 2^(m_old - m_new).
 template <int RB, int NDB>
-__device__ __forceinline__ void maybe_rescale(const float (&tmax)[RB], float (&m_run)[RB],
-                                              float (&l_run)[RB], float (&l_rnd)[RB],
-                                              f32x16 (&acc_o)[RB][NDB]) {
-  bool need = false;
+__device__ __forceinline__ void raise_max(const float (&tmax)[RB], float (&m_run)[RB],
+                                          float (&l_run)[RB], float (&l_rnd)[RB],
+                                          f32x16 (&acc_o)[RB][NDB]) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) need |= tmax[rb] > m_run[rb] + kTau;
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+  for (int rb = 0; rb < RB; ++rb) {
+    const float m_new = fmaxf(m_run[rb], tmax[rb]);
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+    l_run[rb] *= alpha;
+    l_rnd[rb] *= alpha;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float m_new = tmax[rb] > m_run[rb] + kTau ? tmax[rb] : m_run[rb];
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-      l_run[rb] *= alpha;
-      l_rnd[rb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_o[rb][db] *= alpha;
-      m_run[rb] = m_new;
-    }
+    for (int db = 0; db < NDB; ++db) acc_o[rb][db] *= alpha;
+    m_run[rb] = m_new;
   }
 }
 
 // P = 2^(t - m) rounded to the input dtype, packed as the B operand of the
-// P V product; l_run sums P as computed (for lse), l_rnd as rounded (for O).
+// P V product; tsum and trnd are this lane's shares of the tile's row sums
+// of P as computed and as rounded.
 template <int DT, int RB, int NKB>
 __device__ __forceinline__ void tile_probs(const f32x16 (&acc)[RB][NKB], const float (&c_eff)[RB],
-                                           const float (&m_run)[RB], float (&l_run)[RB],
-                                           float (&l_rnd)[RB], u32x4 (&pb)[RB][NKB][2]) {
+                                           const float (&m_run)[RB], float (&tsum)[RB],
+                                           float (&trnd)[RB], u32x4 (&pb)[RB][NKB][2]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    // a row with no unmasked key so far keeps m = -inf; use 0 as its
-    // exponent reference so that no -inf - (-inf) is formed
-    const float m_ref = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+    tsum[rb] = 0.f;
+    trnd[rb] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -350,11 +352,11 @@ __device__ __forceinline__ void tile_probs(const f32x16 (&acc)[RB][NKB], const f
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int r = 8 * h + 2 * w;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r], c_eff[rb], -m_ref));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r + 1], c_eff[rb], -m_ref));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r], c_eff[rb], -m_run[rb]));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r + 1], c_eff[rb], -m_run[rb]));
           const uint32_t pk = Elem<DT>::pack2(p0, p1);
-          l_run[rb] += p0 + p1;
-          l_rnd[rb] = Elem<DT>::add_pair(pk, l_rnd[rb]);
+          tsum[rb] += p0 + p1;
+          trnd[rb] = Elem<DT>::add_pair(pk, trnd[rb]);
           pb[rb][kb][h][w] = pk;
         }
   }
@@ -366,37 +368,34 @@ __device__ __forceinline__ void tile_probs(const f32x16 (&acc)[RB][NKB], const f
 //   phase 1, one step per 16-wide k-step of the scores of tile j + 1: the RB
 //     matrix ops of that k-step (its K operand read PFK steps ahead) beside
 //     the next PPS probability pairs of tile j on the vector unit;
+//   the lazy-rescale test on tile j's sums of P (and, rarely, the redo);
 //   phase 2, one step per (key block, half, head-dim block) of the P V
-//     product of tile j: its RB matrix ops (V^T operands read PFV steps
-//     ahead) beside a slice of tile j + 1's row max.
+//     product of tile j: its RB matrix ops, V^T operands read PFV steps
+//     ahead.
 // Probability pairs come in the order the P V steps consume them.
 template <int D, int DT, int RB, int NKB>
 __device__ __forceinline__ void pipeline_block(
     const unsigned char* smem, uint32_t k_stage, uint32_t v_stage, uint32_t k_lane, uint32_t vt_x,
     const u32x4 (&qf)[RB][D / 16], const f32x16 (&cur)[RB][NKB], const float (&ce_cur)[RB],
-    const float (&m_run)[RB], float (&l_run)[RB], float (&l_rnd)[RB], f32x16 (&nxt)[RB][NKB],
-    float (&mx_nxt)[RB], f32x16 (&acc_o)[RB][D / 32]) {
+    float (&m_run)[RB], float (&l_run)[RB], float (&l_rnd)[RB], f32x16 (&nxt)[RB][NKB],
+    f32x16 (&acc_o)[RB][D / 32]) {
   using E = Elem<DT>;
   constexpr int CPR = D / 8, NDS = D / 16, NDB = D / 32;
   constexpr int NS1 = NKB * NDS;                   // phase-1 steps
   constexpr int NPAIR = RB * NKB * 8;              // probability pairs per lane
   constexpr int PPS = (NPAIR + NS1 - 1) / NS1;     // pairs per phase-1 step
   constexpr int NS2 = NKB * 2 * NDB;               // phase-2 steps
-  constexpr int NMAX = RB * NKB * 8;               // max3 folds of tile j + 1
-  constexpr int MPS = (NMAX + NS2 - 1) / NS2;      // folds per phase-2 step
   constexpr int PFK = 3, PFV = 2;                  // operand read-ahead (steps)
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) nxt[rb][kb] = f32x16{};
-  float m_ref[RB];
+  float tsum[RB], trnd[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    // a row with no unmasked key so far keeps m = -inf; use 0 as its
-    // exponent reference so that no -inf - (-inf) is formed
-    m_ref[rb] = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-    mx_nxt[rb] = -INFINITY;
+    tsum[rb] = 0.f;
+    trnd[rb] = 0.f;
   }
 
   // phase 1
@@ -424,17 +423,19 @@ __device__ __forceinline__ void pipeline_block(
       if (p < NPAIR) {
         const int w = p % 4, rb = (p / 4) % RB, h = (p / (4 * RB)) % 2, pkb = p / (8 * RB);
         const int r = 8 * h + 2 * w;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[rb][pkb][r], ce_cur[rb], -m_ref[rb]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[rb][pkb][r + 1], ce_cur[rb], -m_ref[rb]));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[rb][pkb][r], ce_cur[rb], -m_run[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[rb][pkb][r + 1], ce_cur[rb], -m_run[rb]));
         const uint32_t pk = E::pack2(p0, p1);
-        l_run[rb] += p0 + p1;
-        l_rnd[rb] = E::add_pair(pk, l_rnd[rb]);
+        tsum[rb] += p0 + p1;
+        trnd[rb] = E::add_pair(pk, trnd[rb]);
         pb[rb][pkb][h][w] = pk;
       }
     }
   }
 
-  // phase 2
+  // phase 2 operand reads, then the lazy-rescale test: every P of this lane
+  // is at most its tsum, so tsum <= kSumLimit in all lanes bounds all of P.
+  // Otherwise (rarely) raise m to the tile's row max and redo the tile's P.
   const unsigned char* v_lds = smem + v_stage;
   auto v_read = [&](int st) {
     const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
@@ -448,6 +449,40 @@ __device__ __forceinline__ void pipeline_block(
 #pragma unroll
   for (int i = 0; i < PFV; ++i)
     if (i < NS2) vq[i] = v_read(i);
+  bool big = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) big |= !(tsum[rb] <= kSumLimit);
+  if (__builtin_amdgcn_ballot_w64(big) != 0) {
+    float tm[RB], m_old[RB], ts2[RB], tr2[RB];
+    u32x4 pb2[RB][NKB][2];
+    tile_max<RB, NKB>(cur, ce_cur, tm);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) m_old[rb] = m_run[rb];
+    raise_max<RB, NDB>(tm, m_run, l_run, l_rnd, acc_o);
+    tile_probs<DT, RB, NKB>(cur, ce_cur, m_run, ts2, tr2, pb2);
+    // rows whose m did not move keep the P already computed (the same
+    // values); selecting rather than overwriting keeps the phase-1 packing
+    // of P where it is instead of letting it sink past this test
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool moved = m_run[rb] != m_old[rb];
+      tsum[rb] = moved ? ts2[rb] : tsum[rb];
+      trnd[rb] = moved ? tr2[rb] : trnd[rb];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pb[rb][kb][h][w] = moved ? pb2[rb][kb][h][w] : pb[rb][kb][h][w];
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    l_run[rb] += tsum[rb];
+    l_rnd[rb] += trnd[rb];
+  }
+
+  // phase 2
 #pragma unroll
   for (int st = 0; st < NS2; ++st) {
     const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
@@ -455,14 +490,6 @@ __device__ __forceinline__ void pipeline_block(
     if (st + PFV < NS2) vq[st % PFV] = v_read(st + PFV);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = E::mfma(a, pb[rb][kb][h], acc_o[rb][db]);
-#pragma unroll
-    for (int mm = 0; mm < MPS; ++mm) {
-      const int f = st * MPS + mm;  // fold f = (rb * NKB + kb) * 8 + i
-      if (f < NMAX) {
-        const int i = f % 8, fkb = (f / 8) % NKB, rb = f / (8 * NKB);
-        mx_nxt[rb] = fmaxf(fmaxf(mx_nxt[rb], nxt[rb][fkb][2 * i]), nxt[rb][fkb][2 * i + 1]);
-      }
-    }
   }
 }
 
@@ -540,13 +567,12 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[rb][db] = f32x16{};
-  // Per row (this lane's share of its keys): the reference max m of t
-  // (base-2), the sum of P as computed (for lse), and the sum of P as
-  // rounded for the P V product (normalises O).
+  // Per row: the reference max m of t (base-2) and this lane's shares of the
+  // row sums of P as computed (for lse) and as rounded (normalises O).
   float m_run[RB], l_run[RB], l_rnd[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
+    m_run[rb] = 0.f;
     l_run[rb] = 0.f;
     l_rnd[rb] = 0.f;
   }
@@ -560,7 +586,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
 
   // Software pipeline. Iteration j computes the scores of tile j + 1 on the
   // matrix cores while the vector unit turns tile j's scores into P, then the
-  // P V product of tile j while the vector unit takes tile j + 1's row max.
+  // P V product of tile j.
   // At its top every load issued in iteration j - 1 (K of tile j + 1, V of
   // tile j) has landed, and after the barrier every wave is done with
   // iteration j - 1, so K of tile j + 2 goes into tile j's K stage and V of
@@ -574,11 +600,11 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
   wait_vm_lgkm0<0>();
   workgroup_barrier();
   if (n_act > 0) {
-    float tm[RB];
+    // m starts at the row max of tile 0, which holds an unmasked key for
+    // every row (key 0), so m is finite from here on
     tile_scores<D, DT, RB, NKB>(smem, kK0, k_lane, qf, s_a);
     tile_mask<RB, NKB, CAUSAL>(s_a, 0, wave_row0, S, c, l32, hi, ce_a);
-    tile_max<RB, NKB>(s_a, ce_a, tm);
-    maybe_rescale<RB, NDB>(tm, m_run, l_run, l_rnd, acc_o);
+    tile_max<RB, NKB>(s_a, ce_a, m_run);
   }
 
   // One pipeline step for tile j with parity PAR = j % 2 (known at compile
@@ -596,26 +622,18 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
     if (j + 2 < n_tiles) load_tile<LPW, TB>(k_head, head_bytes, j + 2, smem + k_free, wave, k_off);
     if (j + 1 < n_tiles) load_tile<LPW, TB>(v_head, head_bytes, j + 1, smem + v_free, wave, v_off);
     if (j < n_act) {
-      // scores of tile j + 1 || probabilities of tile j, then P V of tile j ||
-      // row max of tile j + 1 (past the wave's last tile the scores come from a
-      // stale stage and are never used)
-      float mx[RB];
+      // scores of tile j + 1 || probabilities of tile j, then P V of tile j
+      // (past the wave's last tile the scores come from a stale stage and are
+      // never used)
       pipeline_block<D, DT, RB, NKB>(smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run,
-                                     l_run, l_rnd, nxt, mx, acc_o);
+                                     l_run, l_rnd, nxt, acc_o);
       if (j + 1 < n_act) {
-        float tm[RB];
         if (tile_needs_mask<RB, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S)) {
-          // boundary tile: mask, then take the max again
           tile_mask<RB, NKB, CAUSAL>(nxt, (j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
-          tile_max<RB, NKB>(nxt, ce_nxt, tm);
         } else {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            ce_nxt[rb] = c;
-            tm[rb] = xor32_max(mx[rb]) * c;
-          }
+          for (int rb = 0; rb < RB; ++rb) ce_nxt[rb] = c;
         }
-        maybe_rescale<RB, NDB>(tm, m_run, l_run, l_rnd, acc_o);
       }
     }
   };
@@ -624,9 +642,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
     if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1, s_b, ce_b, s_a, ce_a);
   }
 
-  // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, which
-  // makes O an exact convex combination of V rows; lse = ln2 (m + log2 l)
-  // from the unrounded sum.
+  // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, and
+  // lse = ln2 (m + log2 l) from the unrounded sum.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = wave_row0 + 32 * rb + l32;
