@@ -91,6 +91,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile sum of P
+// Phase-1 k-steps between this wave's tile-load blocks (0: all at the start
+// of the step). Spacing them out helps D = 128 slightly; D = 64 and D = 256
+// run best with all loads up front.
+template <int D> struct LoadEvery { static constexpr int kValue = D == 128 ? 2 : 0; };
 
 // Buffer resource word 3 for raw (unswizzled, stride 0) buffers on gfx9.
 constexpr int kBufferFlags = 0x00020000;
@@ -221,25 +225,58 @@ __device__ __forceinline__ void tile_load_offsets(int wave, int lane, uint32_t (
   }
 }
 
-// Start loading tile t of a head (K or V) into LDS at `dst`: this wave's LPW
-// 1 KiB blocks. The buffer is rebased on the tile, so its record count ends
-// at the end of the head and loads past S return zero.
+// Buffer descriptor for tile t of a head (K or V), rebased on the tile. Its
+// record count ends at `limit` bytes from the head start (the end of the
+// head, so that loads past S return zero; 0 for a tile that is not needed,
+// whose loads then all return zero).
+template <int TB>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned char* head_base,
+                                                            uint32_t limit, int t) {
+  // both values are wave-uniform; readfirstlane keeps them (and so the buffer
+  // descriptor) in scalar registers
+  const uint32_t start = (uint32_t)t * TB;
+  const uint32_t left = (uint32_t)wave_uniform((int)(limit - (start < limit ? start : limit)));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + start), 0, (int)left, kBufferFlags);
+}
+
+// Block i (of this wave's LPW) of a tile load into LDS at `dst`: 64 lanes x
+// 16 bytes into the 1 KiB block (wave * LPW + i) of the stage.
+template <int LPW>
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst,
+                                           int wave, uint32_t off, int i) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * LPW + i) * 1024), 16,
+                                           off, 0, 0, 0);
+}
+
+// Start loading a whole tile (this wave's LPW blocks).
 template <int LPW, int TB>
 __device__ __forceinline__ void load_tile(const unsigned char* head_base, uint32_t head_bytes,
                                           int t, unsigned char* dst, int wave,
                                           const uint32_t* off) {
-  // both values are wave-uniform; readfirstlane keeps them (and so the buffer
-  // descriptor) in scalar registers
-  const uint32_t start = (uint32_t)t * TB;
-  const uint32_t left =
-      (uint32_t)wave_uniform((int)(head_bytes - (start < head_bytes ? start : head_bytes)));
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + start), 0, (int)left, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc<TB>(head_base, head_bytes, t);
 #pragma unroll
-  for (int i = 0; i < LPW; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * LPW + i) * 1024), 16,
-                                             off[i], 0, 0, 0);
+  for (int i = 0; i < LPW; ++i) load_block<LPW>(rsrc, dst, wave, off[i], i);
 }
+
+// The loads one pipeline step issues: this wave's LPW blocks of the next K
+// tile, then its LPW blocks of the next V tile, issued one at a time between
+// the step's matrix ops (or all at its start) so that the waves of a compute
+// unit do not all queue their loads at once.
+template <int LPW>
+struct StepLoads {
+  __amdgpu_buffer_rsrc_t k_rsrc, v_rsrc;
+  unsigned char* k_dst;
+  unsigned char* v_dst;
+  const uint32_t* k_off;
+  const uint32_t* v_off;
+  int wave;
+  __device__ __forceinline__ void issue(int n) const {
+    if (n < LPW)
+      load_block<LPW>(k_rsrc, k_dst, wave, k_off[n], n);
+    else
+      load_block<LPW>(v_rsrc, v_dst, wave, v_off[n - LPW], n - LPW);
+  }
+};
 
 // S^T = K_t Q^T for one tile whose K sits at byte k_stage of LDS. Chunk
 // (2 s + hi) ^ x of a key row (x = swz_k(row)) is byte offset
@@ -373,9 +410,10 @@ __device__ __forceinline__ void tile_probs(const f32x16 (&acc)[RB][NKB], const f
 //     product of tile j: its RB matrix ops, V^T operands read PFV steps
 //     ahead.
 // Probability pairs come in the order the P V steps consume them.
-template <int D, int DT, int RB, int NKB>
+template <int D, int DT, int RB, int NKB, int LPW, int LEVERY>
 __device__ __forceinline__ void pipeline_block(
-    const unsigned char* smem, uint32_t k_stage, uint32_t v_stage, uint32_t k_lane, uint32_t vt_x,
+    const StepLoads<LPW>& ld, const unsigned char* smem, uint32_t k_stage, uint32_t v_stage,
+    uint32_t k_lane, uint32_t vt_x,
     const u32x4 (&qf)[RB][D / 16], const f32x16 (&cur)[RB][NKB], const float (&ce_cur)[RB],
     float (&m_run)[RB], float (&l_run)[RB], float (&l_rnd)[RB], f32x16 (&nxt)[RB][NKB],
     f32x16 (&acc_o)[RB][D / 32]) {
@@ -413,6 +451,16 @@ __device__ __forceinline__ void pipeline_block(
 #pragma unroll
   for (int st = 0; st < NS1; ++st) {
     const int kb = st / NDS, s = st % NDS;
+    if (LEVERY == 0) {
+      if (st == 0)
+#pragma unroll
+        for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
+    } else if (st % LEVERY == 0 && st / LEVERY < 2 * LPW) {
+      ld.issue(st / LEVERY);
+      // keep each load in its own k-step: vector, scalar and LDS instructions
+      // may be scheduled across this point, matrix ops and memory loads not
+      __builtin_amdgcn_sched_barrier(0x786);
+    }
     const u32x4 a = kq[st % PFK];
     if (st + PFK < NS1) kq[st % PFK] = k_read(st + PFK);
 #pragma unroll
@@ -619,14 +667,18 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
     constexpr uint32_t v_free = PAR ? kV0 : kV1;  // V of tile j - 1 (done)
     wait_vm_lgkm0<0>();
     workgroup_barrier();
-    if (j + 2 < n_tiles) load_tile<LPW, TB>(k_head, head_bytes, j + 2, smem + k_free, wave, k_off);
-    if (j + 1 < n_tiles) load_tile<LPW, TB>(v_head, head_bytes, j + 1, smem + v_free, wave, v_off);
+    // K of tile j + 2 and V of tile j + 1; a tile past the workgroup's last
+    // gets a zero-length buffer, so its loads only write zeros to a free stage
+    const StepLoads<LPW> ld{
+        tile_rsrc<TB>(k_head, j + 2 < n_tiles ? head_bytes : 0u, j + 2),
+        tile_rsrc<TB>(v_head, j + 1 < n_tiles ? head_bytes : 0u, j + 1),
+        smem + k_free, smem + v_free, k_off, v_off, wave};
     if (j < n_act) {
       // scores of tile j + 1 || probabilities of tile j, then P V of tile j
       // (past the wave's last tile the scores come from a stale stage and are
       // never used)
-      pipeline_block<D, DT, RB, NKB>(smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run,
-                                     l_run, l_rnd, nxt, acc_o);
+      pipeline_block<D, DT, RB, NKB, LPW, LoadEvery<D>::kValue>(
+          ld, smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt, acc_o);
       if (j + 1 < n_act) {
         if (tile_needs_mask<RB, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S)) {
           tile_mask<RB, NKB, CAUSAL>(nxt, (j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
@@ -635,12 +687,18 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
           for (int rb = 0; rb < RB; ++rb) ce_nxt[rb] = c;
         }
       }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
     }
   };
   for (int j = 0; j < n_tiles; j += 2) {
     step(std::integral_constant<int, 0>{}, j, s_a, ce_a, s_b, ce_b);
     if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1, s_b, ce_b, s_a, ce_a);
   }
+  // the last steps' loads (zeros into free stages) must land before the
+  // workgroup's LDS is released
+  wait_vm_lgkm0<0>();
 
   // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, and
   // lse = ln2 (m + log2 l) from the unrounded sum.
