@@ -74,6 +74,43 @@ def test_peaky_small_full(dtype):
     assert_parity(o, lse, o_ref, lse_ref, dtype, "peaky small")
 
 
+def _ramp_inputs(S, D, dtype, direction, seed):
+    """Scores that climb steeply along the keys (direction +1) or fall
+    (direction -1): every query has q[0] = 8 and key j has k[j, 0] growing
+    linearly with j, so the base-2 logit of the last keys exceeds that of the
+    first tile by about 60. Other components are small N(0, 0.25^2) noise;
+    v is N(0, 1). Rounded once to the dtype, like every other input."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(1, 2, S, D, generator=g) * 0.25
+    k = torch.randn(1, 2, S, D, generator=g) * 0.25
+    v = torch.randn(1, 2, S, D, generator=g)
+    c = 1.4426950408889634 / D ** 0.5
+    amp = 60.0 / (8.0 * c)
+    ramp = torch.arange(S, dtype=torch.float32) / S * amp
+    q[..., 0] = 8.0
+    k[..., 0] = ramp if direction > 0 else ramp.flip(0)
+    td = torch.float16 if dtype == "f16" else torch.bfloat16
+    return q.to(td), k.to(td), v.to(td)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_rising_scores_force_rescale(D, dtype):
+    """Later key tiles score far above the first one, so the kernel's lazy
+    reference max must be raised mid-sequence (the redo path of a tile whose
+    row sum of P passes 2^12), repeatedly; a falling ramp never raises it."""
+    for causal in (False, True):
+        for direction in (1, -1):
+            S = 700
+            announce(f"ramp D={D} {dtype} causal={causal} direction={direction}")
+            q, k, v = _ramp_inputs(S, D, dtype, direction, seed=11 + D)
+            scale = 1.0 / D ** 0.5
+            o, lse = run_gpu(q, k, v, causal, scale)
+            o_ref, lse_ref = oracle_full(q, k, v, causal, scale)
+            assert_parity(o, lse, o_ref, lse_ref, dtype,
+                          f"ramp D{D} {dtype} causal={causal} dir={direction}")
+
+
 def test_scale_values():
     """Scale 0 (uniform weights), a large scale, and a non-default value."""
     for scale in (0.0, 0.5, 1.0 / 3.0):
