@@ -59,7 +59,7 @@ def read_traffic(workload_name: str):
         return None
 
 
-def time_gpu(w, steps: int, warmup: int):
+def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0):
     import torch
 
     import flashattention_tiled_amd as fa
@@ -84,6 +84,13 @@ def time_gpu(w, steps: int, warmup: int):
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize(dev)
+    # the GPU clock ramps up over tens of milliseconds of work: short launches
+    # keep warming up until `warmup_min_s` of launches have run
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < warmup_min_s:
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize(dev)
 
     # per-launch HIP events on the launch stream, plus wall clock over the steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -167,7 +174,7 @@ def run_table(path: str, steps: int, warmup: int):
 
     rows = []
     for w in wl.ALL:
-        r = time_gpu(w, steps, warmup)
+        r = time_gpu(w, steps, warmup, warmup_min_s=0.3)
         avg, med = stats_line(w, r)
         tf = w.flops / (med * 1e-3) / 1e12
         gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9

@@ -545,7 +545,7 @@ template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, float c /* scale * log2(e) */) {
+    int S, float c /* scale * log2(e) */, int pair_split) {
   using SH = Shape<D>;
   using E = Elem<DT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
@@ -566,12 +566,17 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
   // Workgroup -> (query tile, batch*head). Tiles are taken in descending
   // query-tile order across all heads, so under causal masking the longest
   // tiles start first; the workgroups of one (b, h) are H*B apart in launch
-  // order, which keeps them on one XCD when H*B is a multiple of 8.
+  // order, which keeps them on one XCD when H*B is a multiple of 8. When the
+  // whole causal grid is resident at once (pair_split > 0, set by the host),
+  // the workgroups from pair_split on take the query tiles in ascending
+  // order instead, so that the second workgroup a compute unit receives is
+  // a light tile beside its heavy first one.
   const int n_qt = gridDim.x;
   const int n_bh = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int bh = lin % n_bh;
-  const int qt = n_qt - 1 - lin / n_bh;
+  const int qt = (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh
+                                                       : n_qt - 1 - lin / n_bh;
   const int q0 = qt * Br;
   const size_t head = (size_t)bh * (size_t)S * D;
   const int wave_row0 = q0 + wave * SH::kRowsPerWave;
@@ -724,30 +729,38 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
 
 template <int D, int DT, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                  int H, int S, float scale, hipStream_t stream) {
+                  int H, int S, float scale, int n_cu, hipStream_t stream) {
   using SH = Shape<D>;
-  const dim3 grid((unsigned)((S + SH::kBr - 1) / SH::kBr), (unsigned)H, (unsigned)B);
+  const int n_qt = (S + SH::kBr - 1) / SH::kBr;
+  const dim3 grid((unsigned)n_qt, (unsigned)H, (unsigned)B);
   const dim3 block(SH::kThreads);
+  // workgroups resident per compute unit: the register budget allows
+  // kWavesPerSimd waves per SIMD, i.e. that many 4-wave workgroups
+  const long long slots = (long long)n_cu * Tile<D>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long n_wg = (long long)n_qt * H * B;
+  const int pair_split =
+      (CAUSAL && n_qt > 1 && n_wg <= slots) ? (int)(((n_qt + 1) / 2) * (long long)H * B) : 0;
   fa2_fwd_kernel<D, DT, CAUSAL><<<grid, block, 0, stream>>>(
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
-      scale * kLog2e);
+      scale * kLog2e, pair_split);
   return hipGetLastError();
 }
 
 template <int D, int DT>
 hipError_t launch_causal(int causal, const void* q, const void* k, const void* v, void* o,
-                         float* lse, int B, int H, int S, float scale, hipStream_t stream) {
-  return causal ? launch<D, DT, true>(q, k, v, o, lse, B, H, S, scale, stream)
-                : launch<D, DT, false>(q, k, v, o, lse, B, H, S, scale, stream);
+                         float* lse, int B, int H, int S, float scale, int n_cu,
+                         hipStream_t stream) {
+  return causal ? launch<D, DT, true>(q, k, v, o, lse, B, H, S, scale, n_cu, stream)
+                : launch<D, DT, false>(q, k, v, o, lse, B, H, S, scale, n_cu, stream);
 }
 
 template <int D>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
-                        void* o, float* lse, int B, int H, int S, float scale,
+                        void* o, float* lse, int B, int H, int S, float scale, int n_cu,
                         hipStream_t stream) {
   return dtype == FA2_F16
-             ? launch_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, S, scale, stream)
-             : launch_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, S, scale, stream);
+             ? launch_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, S, scale, n_cu, stream)
+             : launch_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, S, scale, n_cu, stream);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -755,11 +768,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Per-device verdict on whether the device is gfx950: 0 unknown, 1 yes, 2 no.
+// Per-device verdict on whether the device is gfx950 (0 unknown, 1 yes,
+// 2 no) and its compute-unit count, both cached on first use.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];
+std::atomic<int> g_device_cus[kMaxDevices];
 
-int check_device() {
+int check_device(int* n_cu) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -773,8 +788,11 @@ int check_device() {
       return FA2_ERR_NO_DEVICE;
     }
     verdict = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                            std::memory_order_relaxed);
     g_device_ok[dev].store(verdict, std::memory_order_release);
   }
+  *n_cu = g_device_cus[dev].load(std::memory_order_relaxed);
   return verdict == 1 ? FA2_OK : FA2_ERR_NO_DEVICE;
 }
 
@@ -837,16 +855,21 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, flo
       overlaps(lse, lse_bytes, k, tensor_bytes) || overlaps(lse, lse_bytes, v, tensor_bytes) ||
       overlaps(lse, lse_bytes, o, tensor_bytes))
     return FA2_ERR_ALIAS;
-  const int dev = check_device();
+  int n_cu = 0;
+  const int dev = check_device(&n_cu);
   if (dev != FA2_OK) return dev;
 
   (void)hipGetLastError();  // start from a clean error state
   hipStream_t st = (hipStream_t)stream;
   hipError_t err;
   switch (D) {
-    case 64: err = launch_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st); break;
-    case 128: err = launch_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st); break;
-    default: err = launch_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st); break;
+    case 64: err = launch_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st); break;
+    case 128:
+      err = launch_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st);
+      break;
+    default:
+      err = launch_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st);
+      break;
   }
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
