@@ -42,14 +42,26 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def library_sha() -> str:
+    import flashattention_tiled_amd as fa
+    try:
+        with open(fa.LIB_PATH, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return ""
+
+
 def read_traffic(workload_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on this workload with the current kernel source; else None."""
+    was taken on this workload with the kernel that is built now (the same
+    source, or a bit-identical library); else None."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     text = open(TRAFFIC_SUMMARY).read()
     fields = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", text, flags=re.M))
-    if fields.get("kernel_source_sha256") != kernel_source_sha():
+    same_source = fields.get("kernel_source_sha256") == kernel_source_sha()
+    same_library = fields.get("library_sha256", "-") == library_sha()
+    if not (same_source or same_library):
         return None
     if fields.get("workload") != workload_name:
         return None

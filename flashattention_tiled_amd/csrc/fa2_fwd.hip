@@ -424,6 +424,8 @@ __device__ __forceinline__ void pipeline_block(
   constexpr int PPS = (NPAIR + NS1 - 1) / NS1;     // pairs per phase-1 step
   constexpr int NS2 = NKB * 2 * NDB;               // phase-2 steps
   constexpr int PFK = 3, PFV = 2;                  // operand read-ahead (steps)
+  static_assert(LEVERY == 0 || (NS1 + LEVERY - 1) / LEVERY >= 2 * LPW,
+                "the load spacing must leave a k-step for every load block");
 
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
