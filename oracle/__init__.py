@@ -14,7 +14,10 @@ What it follows (the pages' statement of the problem):
     attention that FlashAttention-2 reproduces exactly, infra.bea.ai guide
     introduction);
   * lse_i = m_i + ln l_i (the per-row logsumexp of the FlashAttention-2
-    epilogue, jared-hpc Lecture 6 reading task).
+    epilogue, jared-hpc Lecture 6 reading task);
+  * a KV-cache form with Sq queries against Sk keys, the queries being the
+    last Sq positions (causal keeps j <= i + Sk - Sq), for the decoding
+    variant the infra.bea.ai guide names ("When V2 Is Used vs Not").
 
 Inputs are numpy fp64 arrays holding exactly the values the GPU receives.
 """
@@ -58,6 +61,8 @@ def _load():
         lib.oracle_attention_rows_f64.argtypes = [dp, dp, dp, lp, L, dp, dp,
                                                    L, L, L, L, I, D, I]
         lib.oracle_attention_rows_f64.restype = I
+        lib.oracle_attention_kv_f64.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, I, D, I]
+        lib.oracle_attention_kv_f64.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -117,4 +122,26 @@ def attention_rows_f64(q, k, v, rows, causal: bool, scale: float, nthreads: int 
                                            int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_rows_f64 failed with code {rc}")
+    return o, lse
+
+
+def attention_kv_f64(q, k, v, causal: bool, scale: float, nthreads: int = 0):
+    """Sq queries against Sk keys per head (the KV-cache form): q (B,H,Sq,D),
+    k and v (B,H,Sk,D). Causal keeps key j for query i iff j <= i + Sk - Sq.
+
+    Returns (o (B,H,Sq,D), lse (B,H,Sq)), both fp64.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q (B,H,Sq,D), k and v (B,H,Sk,D): {q.shape} {k.shape} {v.shape}")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    o = np.empty((B, H, Sq, D), np.float64)
+    lse = np.empty((B, H, Sq), np.float64)
+    rc = _load().oracle_attention_kv_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                         B, H, Sq, Sk, D, int(bool(causal)), float(scale),
+                                         int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_kv_f64 failed with code {rc}")
     return o, lse

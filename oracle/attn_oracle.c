@@ -161,6 +161,89 @@ int oracle_attention_rows_f64(const double *q, const double *k,
     return failed ? 3 : 0;
 }
 
+/*
+ * Attention of Sq query rows against Sk key rows per head: the decoding
+ * (KV-cache) form that the infra.bea.ai FlashAttention V2 guide lists as
+ * served by a FlashDecoding variant ("When V2 Is Used vs Not" table).
+ *
+ * q and o are contiguous (B, H, Sq, D); k and v are contiguous (B, H, Sk, D);
+ * lse is contiguous (B, H, Sq). The queries are the last Sq positions of a
+ * sequence whose Sk keys are all present (the cache includes the new rows),
+ * so query i sits at position Sk - Sq + i. Causal masking then keeps key j
+ * for query i iff j <= i + (Sk - Sq): the same "key not after the query"
+ * rule as the cookbook kernel's causal mask, with queries and keys counted
+ * from the same sequence start. With Sq = Sk this is the square case above.
+ * Scores, softmax and lse are as above.
+ */
+static void oracle_one_row_kv(const double *q, const double *k, const double *v,
+                              long H, long Sq, long Sk, long D, long b, long h,
+                              long i, int causal, double scale, double *scores,
+                              double *o_row, double *lse_out) {
+    const double *qi = q + ((b * H + h) * Sq + i) * D;
+    const long kv_head = (b * H + h) * Sk * D;
+    const long n_keys = causal ? i + (Sk - Sq) + 1 : Sk; /* keys j in [0, n_keys) */
+
+    for (long j = 0; j < n_keys; ++j) {
+        const double *kj = k + kv_head + j * D;
+        double dot = 0.0;
+        for (long d = 0; d < D; ++d) dot += qi[d] * kj[d];
+        scores[j] = scale * dot;
+    }
+    double m = -INFINITY;
+    for (long j = 0; j < n_keys; ++j)
+        if (scores[j] > m) m = scores[j];
+    double l = 0.0;
+    for (long j = 0; j < n_keys; ++j) {
+        scores[j] = exp(scores[j] - m);
+        l += scores[j];
+    }
+    for (long d = 0; d < D; ++d) o_row[d] = 0.0;
+    for (long j = 0; j < n_keys; ++j) {
+        const double *vj = v + kv_head + j * D;
+        const double e = scores[j];
+        for (long d = 0; d < D; ++d) o_row[d] += e * vj[d];
+    }
+    for (long d = 0; d < D; ++d) o_row[d] /= l;
+    *lse_out = m + log(l);
+}
+
+/*
+ * Returns 0 on success, 1 for a null pointer, 2 for a non-positive size or
+ * (causal) Sq > Sk, which would leave the first queries without any key,
+ * 3 when a score buffer cannot be allocated.
+ */
+int oracle_attention_kv_f64(const double *q, const double *k, const double *v,
+                            double *o, double *lse, long B, long H, long Sq,
+                            long Sk, long D, int causal, double scale,
+                            int nthreads) {
+    if (!q || !k || !v || !o || !lse) return 1;
+    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || D < 1) return 2;
+    if (causal && Sq > Sk) return 2;
+    const long n_rows = B * H * Sq;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+#endif
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)Sk);
+        if (!scores) {
+            failed = 1;
+        } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 4)
+#endif
+            for (long r = 0; r < n_rows; ++r) {
+                const long i = r % Sq, bh = r / Sq;
+                oracle_one_row_kv(q, k, v, H, Sq, Sk, D, bh / H, bh % H, i, causal,
+                                  scale, scores, o + r * D, lse + r);
+            }
+            free(scores);
+        }
+    }
+    return failed ? 3 : 0;
+}
+
 /* Number of threads an OpenMP region would use by default (1 without OpenMP). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP
