@@ -50,7 +50,8 @@ def _mutant_attn(tmp_path, name, old, new):
         # the row helper needs B for this edit; thread it through its signature
         mutated = mutated.replace("long H, long S, long D, long b, long h, long i,",
                                   "long H, long S, long D, long b, long h, long i, long B,")
-        mutated = mutated.replace("bh / H, bh % H, i, causal,", "bh / H, bh % H, i, B, causal,")
+        mutated = mutated.replace("oracle_one_row(q, k, v, H, S, D, bh / H, bh % H, i, causal,",
+                                  "oracle_one_row(q, k, v, H, S, D, bh / H, bh % H, i, B, causal,")
     c_path = tmp_path / f"{name}.c"
     so_path = tmp_path / f"{name}.so"
     c_path.write_text(mutated)
