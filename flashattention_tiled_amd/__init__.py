@@ -11,7 +11,13 @@ C entry points, re-exported under the same names:
     fa2_supported(D, dtype) -> int
     fa2_status_string(status) -> str
     fa2_rows_per_workgroup(D) -> int
-plus the tensor-level convenience ``attention(q, k, v, causal, scale)``.
+    fa2_fwd_splitkv(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype,
+                    n_split, workspace, workspace_bytes, stream) -> int
+    fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) -> int
+    fa2_splitkv_splits(B, H, Sq, Sk) -> int
+plus the tensor-level conveniences ``attention(q, k, v, causal, scale)`` and
+``attention_splitkv(q, k, v, causal, scale, n_split)`` (Sq queries against Sk
+cached keys).
 """
 from __future__ import annotations
 
@@ -37,8 +43,10 @@ FA2_ERR_SCALE = 6
 FA2_ERR_NO_DEVICE = 7
 FA2_ERR_LAUNCH = 8
 FA2_ERR_ALIAS = 9
+FA2_ERR_WORKSPACE = 10
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_supported", "fa2_status_string", "fa2_rows_per_workgroup")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_supported", "fa2_status_string", "fa2_rows_per_workgroup",
+                    "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits")
 
 
 class FA2Error(RuntimeError):
@@ -70,6 +78,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_rows_per_workgroup.argtypes = [i]
     lib.fa2_rows_per_workgroup.restype = i
+    sz = ctypes.c_size_t
+    lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa2_fwd_splitkv.restype = i
+    lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa2_splitkv_workspace_bytes.restype = sz
+    lib.fa2_splitkv_splits.argtypes = [i, i, i, i]
+    lib.fa2_splitkv_splits.restype = i
     _lib = lib
     return lib
 
@@ -91,6 +106,23 @@ def fa2_status_string(status: int) -> str:
 
 def fa2_rows_per_workgroup(D: int) -> int:
     return int(load_library().fa2_rows_per_workgroup(D))
+
+
+def fa2_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int, Sk: int,
+                    D: int, causal: int, scale: float, dtype: int, n_split: int, workspace: int,
+                    workspace_bytes: int, stream: int) -> int:
+    """Direct call of the split-KV C entry point with raw device addresses."""
+    return int(load_library().fa2_fwd_splitkv(q, k, v, o, lse, B, H, Sq, Sk, D, int(causal),
+                                              float(scale), int(dtype), int(n_split),
+                                              workspace, int(workspace_bytes), stream))
+
+
+def fa2_splitkv_workspace_bytes(B: int, H: int, Sq: int, Sk: int, D: int, n_split: int) -> int:
+    return int(load_library().fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split))
+
+
+def fa2_splitkv_splits(B: int, H: int, Sq: int, Sk: int) -> int:
+    return int(load_library().fa2_splitkv_splits(B, H, Sq, Sk))
 
 
 def _dtype_code(t):
@@ -141,6 +173,59 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         status = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                          lse.data_ptr(), B, H, S, D, int(bool(causal)), float(scale),
                          _dtype_code(q), stream.cuda_stream)
+    if status != FA2_OK:
+        raise FA2Error(status, fa2_status_string(status))
+    return out, lse
+
+
+def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                      n_split: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """O, lse for Sq queries against Sk cached keys: q (B, H, Sq, D), k and v
+    (B, H, Sk, D), contiguous CUDA fp16/bf16 tensors. Causal keeps key j for
+    query i iff j <= i + Sk - Sq (the queries are the last Sq positions).
+    n_split = 0 lets the library pick the number of key chunks. `workspace`
+    may be passed preallocated (a CUDA uint8 tensor of at least
+    fa2_splitkv_workspace_bytes bytes); otherwise one is allocated with torch.
+    Returns (o like q, lse (B, H, Sq) float32). Raises FA2Error on any
+    nonzero status.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] \
+            or q.shape[3] != k.shape[3]:
+        raise ValueError(f"q must be (B, H, Sq, D) and k, v (B, H, Sk, D), got "
+                         f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must have one dtype")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, Sq) tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        if n_split == 0:
+            n_split = fa2_splitkv_splits(B, H, Sq, Sk)
+        need = fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split)
+        if workspace is None:
+            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+        status = fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)),
+                                 float(scale), _dtype_code(q), n_split, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 stream.cuda_stream)
     if status != FA2_OK:
         raise FA2Error(status, fa2_status_string(status))
     return out, lse

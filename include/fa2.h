@@ -27,6 +27,8 @@
 #ifndef FA2_H
 #define FA2_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -50,7 +52,9 @@ typedef enum {
     FA2_ERR_SCALE = 6,     /* scale is negative, NaN or infinite */
     FA2_ERR_NO_DEVICE = 7, /* no current HIP device, or the device is not gfx950 */
     FA2_ERR_LAUNCH = 8,    /* the HIP runtime reported an error at launch */
-    FA2_ERR_ALIAS = 9      /* o or lse overlaps q, k or v, or o overlaps lse */
+    FA2_ERR_ALIAS = 9,     /* o or lse overlaps q, k or v, or o overlaps lse (split-KV:
+                              or the workspace overlaps any tensor) */
+    FA2_ERR_WORKSPACE = 10 /* split-KV: workspace NULL, misaligned or too small */
 } fa2_status;
 
 /*
@@ -97,6 +101,55 @@ const char *fa2_status_string(int status);
  * sequence) for head dimension D; 0 when D is unsupported. The launch grid
  * is (ceil(S / rows), H, B). */
 int fa2_rows_per_workgroup(int D);
+
+/*
+ * Split-KV attention -- the decoding (KV-cache) form: Sq query rows against
+ * Sk key rows per head, the queries being the last Sq positions of the
+ * sequence. The infra.bea.ai FlashAttention V2 guide lists KV-cache
+ * inference as served by a FlashDecoding variant ("When V2 Is Used vs Not");
+ * the split of the key range into parts whose (m, l) are combined at the end
+ * is jared-hpc Lecture 6's "FA2 change 2", here across workgroups, and the
+ * combine is the guide's rescaling algebra ("Optimization 2"):
+ *
+ *     S_i,j = scale * (q_i . k_j), j kept iff !causal or j <= i + (Sk - Sq)
+ *     O_i and lse_i as for fa2_fwd over the kept keys.
+ *
+ * The keys of each (b, h) are cut into n_split chunks of whole 32-key tiles;
+ * one kernel computes each chunk's unnormalised O and its (m, l) into the
+ * workspace, a second merges the chunks:
+ *     M = max_g m_g,  w_g = exp(m_g - M),
+ *     O = sum_g w_g O_g / sum_g w_g l_g,  lse = M + ln(sum_g w_g l_g).
+ *
+ * q, o     (B, H, Sq, D) contiguous, `dtype`, 16-byte aligned.
+ * k, v     (B, H, Sk, D) contiguous, `dtype`, 16-byte aligned.
+ * lse      (B, H, Sq) floats, natural log, 4-byte aligned.
+ * B, H     1..65535 each.  Sq, Sk >= 1; causal requires Sq <= Sk.
+ * D, causal, scale, dtype, stream as for fa2_fwd.
+ * n_split  key chunks per (b, h); 0 picks fa2_splitkv_splits(B, H, Sq, Sk).
+ *          Chunks that would be empty are dropped.
+ * workspace, workspace_bytes
+ *          caller-owned device memory, 16-byte aligned, at least
+ *          fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) bytes. Its
+ *          contents on entry are ignored and it is overwritten; it must not
+ *          overlap any tensor, and two calls in flight at once need two
+ *          workspaces. The library allocates nothing.
+ * Returns an fa2_status (FA2_ERR_WORKSPACE for a missing, misaligned or short
+ * workspace; FA2_ERR_SHAPE also for causal with Sq > Sk). Two kernels are
+ * enqueued on `stream`; the call does not wait for them.
+ */
+int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                    int dtype, int n_split, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fa2_fwd_splitkv needs for these sizes and n_split
+ * (0 = the default split count); 0 for invalid sizes or head dims. */
+size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int n_split);
+
+/* The default number of key chunks per (b, h): enough workgroups to give
+ * every compute unit of the current device several, each chunk at least
+ * four 32-key tiles; 1 for invalid sizes. */
+int fa2_splitkv_splits(int B, int H, int Sq, int Sk);
 
 #ifdef __cplusplus
 }

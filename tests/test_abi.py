@@ -58,7 +58,7 @@ def test_supported_and_rows(lib):
 
 
 def test_status_strings(lib):
-    for s in range(10):
+    for s in range(11):
         assert fa.fa2_status_string(s)
     assert fa.fa2_status_string(0) == "ok"
     assert "unknown" in fa.fa2_status_string(99)
@@ -132,3 +132,82 @@ def test_no_device_status_without_gpu(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; the fake pointers must not be launched on")
     assert _call() == fa.FA2_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# split-KV entry point: (1, 1, Sq=4, 64) queries against Sk=256 keys, D=64
+# ---------------------------------------------------------------------------
+_SQ, _SK, _D = 4, 256, 64
+_NQ, _NKV = _SQ * _D * 2, _SK * _D * 2
+QS, KS, VS, OS, LS, WS = (0x20000000 + i * 0x100000 for i in range(6))
+
+
+def _ws_bytes(n_split):
+    return fa.fa2_splitkv_workspace_bytes(1, 1, _SQ, _SK, _D, n_split)
+
+
+def _call_splitkv(**kw):
+    args = dict(q=QS, k=KS, v=VS, o=OS, lse=LS, B=1, H=1, Sq=_SQ, Sk=_SK, D=_D, causal=0,
+                scale=0.125, dtype=fa.FA2_F16, n_split=4, workspace=WS,
+                workspace_bytes=_ws_bytes(4), stream=None)
+    args.update(kw)
+    return fa.fa2_fwd_splitkv(**args)
+
+
+def test_splitkv_workspace_bytes(lib):
+    # part_o (B*H*n_split*Sq*D floats, rounded up to 256 bytes) + (m, l, l) per row and chunk
+    for B, H, Sq, Sk, D, n in ((1, 1, 1, 100, 64, 1), (2, 3, 5, 999, 128, 7), (1, 2, 33, 64, 256, 3)):
+        o_bytes = B * H * n * Sq * D * 4
+        expect = (o_bytes + 255) // 256 * 256 + B * H * n * Sq * 3 * 4
+        assert fa.fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n) == expect
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 1, 1, 96, 1) == 0
+    assert fa.fa2_splitkv_workspace_bytes(0, 1, 1, 1, 64, 1) == 0
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 1, 1, 64, -1) == 0
+    assert fa.fa2_splitkv_splits(1, 1, 1, 1 << 20) >= 1
+    assert fa.fa2_splitkv_splits(0, 1, 1, 1) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA2_ERR_NULL),
+    (dict(lse=None), fa.FA2_ERR_NULL),
+    (dict(Sq=0), fa.FA2_ERR_SHAPE),
+    (dict(Sk=0), fa.FA2_ERR_SHAPE),
+    (dict(B=65536), fa.FA2_ERR_SHAPE),
+    (dict(n_split=-1), fa.FA2_ERR_SHAPE),
+    (dict(n_split=70000, workspace_bytes=1 << 40), fa.FA2_ERR_SHAPE),
+    (dict(causal=1, Sq=_SK + 1), fa.FA2_ERR_SHAPE),
+    (dict(Sk=2**31 - 1), fa.FA2_ERR_SHAPE),
+    (dict(D=96), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=3), fa.FA2_ERR_DTYPE),
+    (dict(k=KS + 8), fa.FA2_ERR_ALIGN),
+    (dict(lse=LS + 1), fa.FA2_ERR_ALIGN),
+    (dict(scale=float("nan")), fa.FA2_ERR_SCALE),
+    (dict(workspace=None), fa.FA2_ERR_WORKSPACE),
+    (dict(workspace=WS + 4), fa.FA2_ERR_WORKSPACE),
+    (dict(workspace_bytes=_ws_bytes(4) - 1), fa.FA2_ERR_WORKSPACE),
+    (dict(n_split=8), fa.FA2_ERR_WORKSPACE),  # the workspace is sized for 4 chunks
+    (dict(o=QS), fa.FA2_ERR_ALIAS),
+    (dict(lse=KS + _NKV - 4), fa.FA2_ERR_ALIAS),
+    (dict(workspace=VS + 16), fa.FA2_ERR_ALIAS),
+    (dict(workspace=OS), fa.FA2_ERR_ALIAS),
+])
+def test_splitkv_validation_status(lib, kw, status):
+    assert _call_splitkv(**kw) == status
+
+
+def test_splitkv_no_device_status_without_gpu(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call_splitkv() == fa.FA2_ERR_NO_DEVICE
+    assert _call_splitkv(n_split=0) == fa.FA2_ERR_NO_DEVICE
+
+
+def test_attention_splitkv_wrapper_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 1, 2, 64, dtype=torch.float16)
+    kv = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.attention_splitkv(q, kv, kv)  # CPU tensors
+    with pytest.raises(ValueError):
+        fa.attention_splitkv(q, kv, kv[:, :, :4])

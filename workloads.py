@@ -75,6 +75,66 @@ def make_qkv(w: Workload, seed: int = 0):
     return q.to(dt), k.to(dt), v.to(dt)
 
 
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Sq queries against Sk cached keys per head (the KV-cache form)."""
+    name: str
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    dtype: str
+    causal: bool
+    qk_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    @property
+    def flops(self) -> float:
+        """4 * B * H * Sq * Sk * D over every query-key pair (causal drops
+        about Sq^2 / 2 of them, ignored: Sq << Sk)."""
+        return 4.0 * self.B * self.H * self.Sq * self.Sk * self.D
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """K and V read once, Q read once, O written once, lse written once."""
+        kv = 2 * self.B * self.H * self.Sk * self.D * 2
+        qo = 2 * self.B * self.H * self.Sq * self.D * 2
+        return kv + qo + self.B * self.H * self.Sq * 4
+
+
+def make_qkv_decode(w: DecodeWorkload, seed: int = 0):
+    """q (B, H, Sq, D), then k and v (B, H, Sk, D), drawn in that order as
+    fp32 N(0, 1) from one seeded CPU generator, q and k times qk_mult in fp32,
+    then rounded once to the dtype (the recipe of make_qkv with two lengths)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((w.B, w.H, w.Sq, w.D), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.H, w.Sk, w.D), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.H, w.Sk, w.D), generator=g, dtype=torch.float32)
+    if w.qk_mult != 1.0:
+        q = q * w.qk_mult
+        k = k * w.qk_mult
+    dt = w.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+# Decoding against a long KV cache (split-KV path): one new token per
+# sequence, and a speculative/chunked step of 16 new tokens, bf16 and fp16.
+DECODE = [
+    DecodeWorkload("decode_b8_h32_sk32768_d128", 8, 32, 1, 32768, 128, "bf16", True),
+    DecodeWorkload("decode_b1_h32_sk131072_d128", 1, 32, 1, 131072, 128, "f16", True),
+    DecodeWorkload("decode_b4_h32_sq16_sk16384_d128", 4, 32, 16, 16384, 128, "bf16", True),
+]
+
+
 # Tiny exact case: B=1, H=2, S=256, D=64, fp16, causal and non-causal.
 TINY = [
     Workload("tiny_causal", 1, 2, 256, 64, "f16", True),
