@@ -7,6 +7,7 @@ Prints one JSON line on stdout; diagnostics go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --table PATH      # every benchmark shape, one line each
+    python bench.py --decode-table PATH   # split-KV decode shapes, GB/s
 
 Metric: TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal masking, and the
 fraction of the MI355X dense fp16/bf16 matrix-core peak (256 CUs x 2.4 GHz x
@@ -119,6 +120,68 @@ def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0):
     return dict(q=q, k=k, v=v, o=o, lse=lse, wall_s=wall, durs_ms=durs)
 
 
+def time_gpu_splitkv(w, steps: int, warmup_min_s: float):
+    """Per-call HIP-event durations of fa2_fwd_splitkv (both of its kernels)
+    on a decode workload, the workspace allocated before the timed region."""
+    import torch
+
+    import flashattention_tiled_amd as fa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in wl.make_qkv_decode(w, seed=0))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = fa.load_library()
+    n_split = fa.fa2_splitkv_splits(w.B, w.H, w.Sq, w.Sk)
+    need = fa.fa2_splitkv_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, n_split)
+    ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    dtype = fa.FA2_F16 if w.dtype == "f16" else fa.FA2_BF16
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.Sq, w.Sk, w.D, int(w.causal), float(w.scale), dtype, n_split,
+            ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    def launch():
+        st = lib.fa2_fwd_splitkv(*args)
+        if st != 0:
+            raise fa.FA2Error(st, fa.fa2_status_string(st))
+
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < warmup_min_s:
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    return n_split, sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+
+
+def run_decode_table(path: str, steps: int):
+    import workloads as wl
+
+    rows = []
+    for w in wl.DECODE:
+        n_split, durs = time_gpu_splitkv(w, steps, warmup_min_s=0.3)
+        med = durs[len(durs) // 2]
+        avg = sum(durs) / len(durs)
+        gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9
+        line = (f"{w.name},{w.B},{w.H},{w.Sq},{w.Sk},{w.D},{w.dtype},{int(w.causal)},{n_split},"
+                f"{med * 1e3:.1f},{avg * 1e3:.1f},{durs[0] * 1e3:.1f},{gbs:.1f},"
+                f"{100 * gbs / PEAK_HBM_GBS:.2f}")
+        log(line)
+        rows.append(line)
+    with open(path, "w") as f:
+        f.write("workload,B,H,Sq,Sk,D,dtype,causal,n_split,us_median,us_avg,us_min,"
+                "alg_GBps,pct_hbm_peak\n")
+        f.write("\n".join(rows) + "\n")
+
+
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
     """Time the fp64 oracle on a random sample of rows of the same workload
     (about `budget_s` of CPU work) and compare those rows with the GPU output."""
@@ -210,14 +273,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--table", default=None, help="time every benchmark shape into a CSV")
+    ap.add_argument("--decode-table", default=None,
+                    help="time the split-KV path on every decode shape into a CSV")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (`steps` times), to "
                          "calibrate the HBM byte counters against a known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the forward pass on one GPU only; "
-              "runs on more than one GPU are not part of this build", file=sys.stderr)
+        print("bench.py measures the forward pass on one GPU only: the library "
+              "has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -230,6 +295,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.decode_table:
+        run_decode_table(args.decode_table, args.steps)
+        return
     if args.table:
         run_table(args.table, args.steps, args.warmup)
         return

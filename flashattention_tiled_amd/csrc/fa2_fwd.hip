@@ -1015,13 +1015,14 @@ __global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
   if (lane == 0) lse[r] = (mx + __builtin_amdgcn_logf(lsum)) * kLn2;
 }
 
-// Key chunks per (b, h) for a launch: enough workgroups to give every
-// compute unit several (decoding is bandwidth bound and needs many loads in
-// flight), each chunk at least 4 tiles long.
+// Key chunks per (b, h) for a launch: enough workgroups for about two on
+// every compute unit (decoding is bandwidth bound; each one-wave workgroup
+// keeps a K and a V tile in flight), each chunk at least 4 tiles long.
 int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu) {
   const long long n_qblk = (Sq + 31) / 32;
   const long long n_tiles = (Sk + SplitTile<64>::kBc - 1) / SplitTile<64>::kBc;
-  const long long target = 8LL * n_cu;
+  // measured on decode shapes: more, shorter chunks lose bandwidth
+  const long long target = 2LL * n_cu;
   long long want = (target + (long long)B * H * n_qblk - 1) / ((long long)B * H * n_qblk);
   const long long cap = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
   if (want > cap) want = cap;

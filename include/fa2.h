@@ -146,9 +146,9 @@ int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float 
  * (0 = the default split count); 0 for invalid sizes or head dims. */
 size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int n_split);
 
-/* The default number of key chunks per (b, h): enough workgroups to give
- * every compute unit of the current device several, each chunk at least
- * four 32-key tiles; 1 for invalid sizes. */
+/* The default number of key chunks per (b, h): enough workgroups for about
+ * two on every compute unit of the current device, each chunk at least four
+ * 32-key tiles; 1 for invalid sizes. */
 int fa2_splitkv_splits(int B, int H, int Sq, int Sk);
 
 #ifdef __cplusplus
