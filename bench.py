@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "flashattention_tiled_amd", "csrc", "fa2_fwd.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa2_fwd_kernel_sweep_s8192_d128_counters.md")
 
 
@@ -39,8 +38,9 @@ def log(*a):
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    from flashattention_tiled_amd.build import prefill_kernel_sha
+
+    return prefill_kernel_sha()
 
 
 def library_sha() -> str:
@@ -60,7 +60,7 @@ def read_traffic(workload_name: str):
         return None
     text = open(TRAFFIC_SUMMARY).read()
     fields = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", text, flags=re.M))
-    same_source = fields.get("kernel_source_sha256") == kernel_source_sha()
+    same_source = fields.get("kernel_sources_sha256") == kernel_source_sha()
     same_library = fields.get("library_sha256", "-") == library_sha()
     if not (same_source or same_library):
         return None

@@ -1,7 +1,7 @@
 """FlashAttention-2 forward pass for MI355X (gfx950): thin Python binding.
 
 Every step of the forward pass runs in the HIP library ``libfa2.so`` built
-from ``csrc/fa2_fwd.hip``; this module only marshals arguments to its C ABI
+from ``csrc/``; this module only marshals arguments to its C ABI
 (declared in ``include/fa2.h``). PyTorch is used for device memory and
 streams. There is no fallback: if the library is missing, importing the
 binding's functions raises.
@@ -60,15 +60,39 @@ class FA2Error(RuntimeError):
 _lib = None
 
 
+def _hip_runtimes_mapped() -> list:
+    """Paths of the HIP runtime libraries (libamdhip64) mapped into this
+    process (Linux), one per copy."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfa2.so (once). Raises OSError when it has not been built."""
+    """Load libfa2.so (once). Raises OSError when it has not been built.
+
+    The library must share torch's HIP runtime: the device pointers and
+    streams it is given come from torch. torch ships its own libamdhip64 with
+    the same soname as the system one, so torch is imported first and the
+    library's dependency then resolves to torch's copy. Loading it before
+    torch would map a second HIP runtime, on which torch's device and
+    allocations do not exist; that case raises instead of running."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise OSError(f"{path} is missing: build it with flashattention_tiled_amd.build "
                       f"(or __graft_entry__.build()) before use")
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+
     lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise OSError("two HIP runtimes are loaded in this process (" + ", ".join(runtimes) +
+                      "); libfa2.so must share torch's: import torch before loading any "
+                      "other library that links libamdhip64")
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa2_fwd.restype = i

@@ -1,12 +1,20 @@
 """Build the HIP library (libfa2.so) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa2_fwd.hip")
+CSRC = os.path.join(PKG, "csrc")
+# the parts of the library, compiled as the one translation unit fa2_lib.hip
+PARTS = [os.path.join(CSRC, f) for f in
+         ("fa2_lib.hip", "fa2_runtime.hip", "fa2_fwd.hip", "fa2_splitkv.hip", "fa2_tile.h",
+          "fa2_host.h")]
+SOURCES = [os.path.join(CSRC, "fa2_lib.hip")]
+# the files that hold the prefill kernel's (fa2_fwd_kernel's) code
+PREFILL_KERNEL_SOURCES = [os.path.join(CSRC, "fa2_tile.h"), os.path.join(CSRC, "fa2_fwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libfa2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,13 +32,25 @@ HIP_FLAGS = [
 
 
 def build_library(force: bool = True, extra_flags=None) -> str:
-    """Compile csrc/fa2_fwd.hip into libfa2.so next to this file."""
+    """Compile csrc/fa2_lib.hip (which includes the other parts) into libfa2.so
+    next to this file."""
     if force or not os.path.exists(LIB_PATH):
         tmp = LIB_PATH + ".tmp"
-        cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-o", tmp, SRC]
+        cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-o", tmp, *SOURCES]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def prefill_kernel_sha() -> str:
+    """SHA-256 over the prefill kernel's source files (name and bytes of each),
+    which keys measurements taken of that kernel to the code they measured."""
+    h = hashlib.sha256()
+    for path in PREFILL_KERNEL_SOURCES:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 if __name__ == "__main__":

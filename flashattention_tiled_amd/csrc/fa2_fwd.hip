@@ -35,104 +35,22 @@
 // whatever the rounding of P (a near one-hot row then reproduces its V row
 // up to fp32 accumulation, not up to the rounding of its largest P).
 //
-// Matrix-core formulation. The wave computes the transposed products
-//   S^T = K_j Q^T   (A = K_j from LDS,   B = Q^T resident in registers)
-//   O^T = V_j^T P^T (A = V_j^T from LDS, B = P^T straight from S^T's registers)
-// with v_mfma_f32_32x32x16_{f16,bf16}. Output column n of a 32x32 block lives
-// in lane n (mod 32), so each lane holds one query row per 32-row block: the
-// row max and row sum are in-lane reductions plus one exchange with the lane
-// 32 away, and the per-row rescale is a per-lane scalar multiply.
-//
-// MFMA 32x32x16 lane layouts used below (lane l, l32 = l % 32, hi = l / 32):
-//   A (32 x 16): lane l holds row l32, 8 k values of half hi.
-//   B (16 x 32): lane l holds column l32, the same 8 k values.
-//   C (32 x 32): register r of lane l holds row 8*(r/4) + 4*hi + r%4, column l32.
-// Any bijection between (hi, element) and k is valid as long as A and B use
-// the same one, which is how P^T is fed from the S^T accumulator registers:
-// B element e of P^T step (kb, h) is accumulator register 8h + e, that is
-// key 32 kb + 16 h + 8 (e / 4) + 4 hi + e % 4, and the V^T operand gathers
-// the same keys.
-//
-// LDS staging. Tiles arrive by buffer loads that write LDS directly, 16 bytes
-// per lane; a 64-lane load fills 1 KiB of consecutive 16-byte slots, so the
-// layout is chosen by which global chunk each lane fetches. Key rows are
-// row-major with their 16-byte chunks XOR-swizzled per row so that the reads
-// below hit distinct banks. Buffer loads past the end of a head return zero,
-// which zero-fills the keys beyond S of a ragged last tile.
-//   K^T A operand: one 16-byte read of row key, chunk (2 s + hi).
-//   V^T A operand: two ds_read_b64_tr_b16, the gfx950 transposing read. In
-//   each 16-lane group, output lane i element e comes from source lane
-//   4 e + i / 4, element i % 4; sources pointed at 4 key rows x 16 dims return
-//   4 consecutive keys of one dim per lane, the layout the A operand needs.
-#include <hip/hip_runtime.h>
+// The matrix-core formulation, lane layouts and LDS staging shared with
+// the split-KV kernels are described in fa2_tile.h.
 
-#include <atomic>
-#include <cmath>
-#include <type_traits>
-#include <cstdint>
-#include <cstring>
+#include "fa2_tile.h"
+#include "fa2_host.h"
 
-#include "fa2.h"
+using fa2_host::check_device;
+using fa2_host::overlaps;
 
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile sum of P
 // Phase-1 k-steps between this wave's tile-load blocks (0: all at the start
 // of the step). Spacing them out helps D = 128 slightly; D = 64 and D = 256
 // run best with all loads up front.
 template <int D> struct LoadEvery { static constexpr int kValue = D == 128 ? 2 : 0; };
-
-// Buffer resource word 3 for raw (unswizzled, stride 0) buffers on gfx9.
-constexpr int kBufferFlags = 0x00020000;
-
-// Element-type specific pieces: the matrix-core product, the RNE packing of
-// two fp32 values into the input dtype, and the sum of a packed pair.
-template <int DT> struct Elem;
-
-template <> struct Elem<FA2_F16> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    f16x2 h = {(_Float16)lo, (_Float16)hi};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-  // acc + lo + hi of a packed pair, in fp32
-  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
-    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
-  }
-};
-
-template <> struct Elem<FA2_BF16> {
-  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    bf16x2 h = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, h);
-  }
-  static __device__ __forceinline__ float add_pair(uint32_t pair, float acc) {
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-  }
-};
 
 // Tile shape per head dimension.
 //   kWaves      waves per workgroup (they share the LDS rings)
@@ -167,97 +85,6 @@ template <int D> struct Shape {
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-// Chunk swizzles (XOR on the 16-byte chunk index within a key row). gfx950
-// LDS has 64 banks (256 bytes per cycle); a ds_read_b128 serves 16 lanes per
-// cycle and a ds_read_b64_tr_b16 32 lanes, so:
-//   K: 16 lanes read chunk c of 16 consecutive rows -> XOR row & 15 puts
-//      them in 16 distinct 16-byte bank groups (D = 64: two rows share a
-//      256-byte line, so XOR (row / 2) & 7 instead);
-//   V: 32 lanes read chunks 4 db .. 4 db + 3 of 4 consecutive rows -> XOR
-//      4 (row & 3) spreads them over all 16 groups (D = 64: XOR
-//      4 ((row / 2) & 1), rows r and r + 1 already sit in different halves).
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  return D == 64 ? (row >> 1) & 7 : row & 15;
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int row) {
-  return D == 64 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
-}
-
-// s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding; expcnt not waited).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-// x made wave-uniform (scalar register); x must already be equal in all lanes.
-__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ void workgroup_barrier() {
-  __asm__ volatile("s_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ float xor32_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Per-lane byte offsets, within one tile, of the 16-byte chunks this wave
-// loads: LDS slot p = block * 64 + lane of the tile receives chunk
-// (p % CPR) ^ swz(row) of key row p / CPR.
-template <int D, int LPW, bool IS_V>
-__device__ __forceinline__ void tile_load_offsets(int wave, int lane, uint32_t (&off)[LPW]) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int p = (wave * LPW + i) * 64 + lane;
-    const int r = p / CPR, cp = p % CPR;
-    const int c = cp ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
-    off[i] = (uint32_t)((r * D + c * 8) * 2);
-  }
-}
-
-// Buffer descriptor for tile t of a head (K or V), rebased on the tile. Its
-// record count ends at `limit` bytes from the head start (the end of the
-// head, so that loads past S return zero; 0 for a tile that is not needed,
-// whose loads then all return zero).
-template <int TB>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned char* head_base,
-                                                            uint32_t limit, int t) {
-  // both values are wave-uniform; readfirstlane keeps them (and so the buffer
-  // descriptor) in scalar registers
-  const uint32_t start = (uint32_t)t * TB;
-  const uint32_t left = (uint32_t)wave_uniform((int)(limit - (start < limit ? start : limit)));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + start), 0, (int)left, kBufferFlags);
-}
-
-// Block i (of this wave's LPW) of a tile load into LDS at `dst`: 64 lanes x
-// 16 bytes into the 1 KiB block (wave * LPW + i) of the stage.
-template <int LPW>
-__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst,
-                                           int wave, uint32_t off, int i) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * LPW + i) * 1024), 16,
-                                           off, 0, 0, 0);
-}
-
-// Start loading a whole tile (this wave's LPW blocks).
-template <int LPW, int TB>
-__device__ __forceinline__ void load_tile(const unsigned char* head_base, uint32_t head_bytes,
-                                          int t, unsigned char* dst, int wave,
-                                          const uint32_t* off) {
-  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc<TB>(head_base, head_bytes, t);
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) load_block<LPW>(rsrc, dst, wave, off[i], i);
-}
-
 // The loads one pipeline step issues: this wave's LPW blocks of the next K
 // tile, then its LPW blocks of the next V tile, issued one at a time between
 // the step's matrix ops (or all at its start) so that the waves of a compute
@@ -277,31 +104,6 @@ struct StepLoads {
       load_block<LPW>(v_rsrc, v_dst, wave, v_off[n - LPW], n - LPW);
   }
 };
-
-// S^T = K_t Q^T for one tile whose K sits at byte k_stage of LDS. Chunk
-// (2 s + hi) ^ x of a key row (x = swz_k(row)) is byte offset
-// (32 s) ^ (16 (hi ^ x)) within it, and row and stage bases have no bits in
-// common with it, so the address of k-step s is one per-tile base XOR 32 s.
-template <int D, int DT, int RB, int NKB>
-__device__ __forceinline__ void tile_scores(const unsigned char* smem, uint32_t k_stage, uint32_t k_lane,
-                                            const u32x4 (&qf)[RB][D / 16],
-                                            f32x16 (&acc)[RB][NKB]) {
-  constexpr int CPR = D / 8, NDS = D / 16;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) acc[rb][kb] = f32x16{};
-  const uint32_t k_base = k_stage + k_lane;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int s = 0; s < NDS; ++s) {
-      const uint32_t off = (k_base ^ (uint32_t)(32 * s)) + (uint32_t)(kb * 32 * CPR * 16);
-      const u32x4 a = *(const u32x4*)(smem + off);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb][kb] = Elem<DT>::mfma(a, qf[rb][s], acc[rb][kb]);
-    }
-}
 
 // Mask one tile's scores. Register r of key block kb holds key
 // key0 + 32 kb + 8 (r / 4) + 4 hi + r % 4; it is kept iff that key is < S
@@ -338,21 +140,6 @@ __device__ __forceinline__ bool tile_needs_mask(int key0, int row0, int S) {
   return (key0 + Bc > S) || (CAUSAL && key0 + Bc - 1 > row0);
 }
 
-// Each row's tile max of t = c_eff * (masked) scores.
-template <int RB, int NKB>
-__device__ __forceinline__ void tile_max(const f32x16 (&acc)[RB][NKB], const float (&c_eff)[RB],
-                                         float (&tmax)[RB]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[rb][kb][r]), acc[rb][kb][r + 1]);
-    tmax[rb] = xor32_max(mx) * c_eff[rb];
-  }
-}
-
 // Raise each row's reference max to at least its tile max tmax, rescaling
 // O~ and both sums by alpha = 2^(m_old - m_new).
 template <int RB, int NDB>
@@ -368,34 +155,6 @@ __device__ __forceinline__ void raise_max(const float (&tmax)[RB], float (&m_run
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[rb][db] *= alpha;
     m_run[rb] = m_new;
-  }
-}
-
-// P = 2^(t - m) rounded to the input dtype, packed as the B operand of the
-// P V product; tsum and trnd are this lane's shares of the tile's row sums
-// of P as computed and as rounded.
-template <int DT, int RB, int NKB>
-__device__ __forceinline__ void tile_probs(const f32x16 (&acc)[RB][NKB], const float (&c_eff)[RB],
-                                           const float (&m_run)[RB], float (&tsum)[RB],
-                                           float (&trnd)[RB], u32x4 (&pb)[RB][NKB][2]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    tsum[rb] = 0.f;
-    trnd[rb] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r = 8 * h + 2 * w;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r], c_eff[rb], -m_run[rb]));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][kb][r + 1], c_eff[rb], -m_run[rb]));
-          const uint32_t pk = Elem<DT>::pack2(p0, p1);
-          tsum[rb] += p0 + p1;
-          trnd[rb] = Elem<DT>::add_pair(pk, trnd[rb]);
-          pb[rb][kb][h][w] = pk;
-        }
   }
 }
 
@@ -765,352 +524,7 @@ hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, con
              : launch_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, S, scale, n_cu, stream);
 }
 
-// ---------------------------------------------------------------------------
-// Split-KV attention: Sq query rows against Sk key rows per head, the
-// decoding (KV-cache) form that the infra.bea.ai guide says a FlashDecoding
-// variant of FlashAttention-2 serves ("When V2 Is Used vs Not"). The queries
-// are the last Sq positions of the sequence, so causal masking keeps key j
-// for query i iff j <= i + (Sk - Sq).
-//
-// Few queries give few query tiles, so the key range of each (b, h) is cut
-// into chunks that run in parallel; each produces partial softmax state for
-// its keys and a second kernel merges them. That is the split-then-combine
-// structure of jared-hpc Lecture 6 ("FA2 change 2": parts of the KV range
-// computed apart and their (m, l) combined at the end), moved from warps to
-// workgroups. The merge is the guide's rescaling algebra applied across
-// chunks: with M = max_g m_g and w_g = 2^(m_g - M),
-//   O = sum_g w_g O~_g / sum_g w_g l_g,   lse = ln2 (M + log2 sum_g w_g l_g).
-//
-// The partial kernel runs one wave per workgroup: a 32-row query block (rows
-// past Sq are zero and never stored) against one key chunk, streamed through
-// a two-stage LDS ring of 32-key tiles by the wave's own LDS-direct loads.
-// Decoding reads every K/V byte once per 32 queries, so it is bound by
-// memory bandwidth, not by the matrix cores; the kernel keeps the exact
-// running row max per tile (no lazy reference point), which also covers rows
-// that have no key in a chunk (their partial is m = -inf, l = 0).
-//
-// Workspace (caller-owned device memory, fp32):
-//   part_o  [B*H][n_split][Sq][D]   unnormalised O~ of each chunk
-//   part_ml [B*H][n_split][Sq][3]   m (base 2), l (P as computed), l (P as rounded)
-// part_ml starts at the part_o size rounded up to 256 bytes.
-template <int D> struct SplitTile {
-  static constexpr int kBc = 32;
-  static constexpr int kTileBytes = kBc * D * 2;
-  static constexpr int kLoadsPerWave = kTileBytes / 1024;  // one wave loads the whole tile
-  static constexpr int kLdsBytes = 4 * kTileBytes;         // K and V, two stages each
-};
-
-size_t splitkv_part_o_bytes(int B, int H, int Sq, int D, int n_split) {
-  const size_t b = (size_t)B * H * n_split * Sq * D * sizeof(float);
-  return (b + 255) / 256 * 256;
-}
-size_t splitkv_workspace_bytes(int B, int H, int Sq, int D, int n_split) {
-  return splitkv_part_o_bytes(B, H, Sq, D, n_split) + (size_t)B * H * n_split * Sq * 3 * sizeof(float);
-}
-
-// Scale every score of the tile and mask keys at or past `lim` (this lane's
-// row keeps keys < lim), in the scaled domain.
-template <int NKB>
-__device__ __forceinline__ void tile_mask_lim(f32x16 (&acc)[1][NKB], int key0, int lim, float c,
-                                              int hi) {
-  const int rel_lim = lim - (key0 + 4 * hi);
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rel = 32 * kb + 8 * (r / 4) + (r % 4);
-      acc[0][kb][r] = rel < rel_lim ? acc[0][kb][r] * c : -INFINITY;
-    }
-}
-
-// O~ += P V for one tile (V at v_stage), V^T operands read two steps ahead.
-template <int D, int DT, int RB, int NKB>
-__device__ __forceinline__ void tile_pv(const unsigned char* smem, uint32_t v_stage, uint32_t vt_x,
-                                        const u32x4 (&pb)[RB][NKB][2],
-                                        f32x16 (&acc_o)[RB][D / 32]) {
-  using E = Elem<DT>;
-  constexpr int CPR = D / 8, NDB = D / 32;
-  constexpr int NS2 = NKB * 2 * NDB;
-  constexpr int PFV = 2;
-  const unsigned char* v_lds = smem + v_stage;
-  auto v_read = [&](int st) {
-    const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
-    const unsigned char* vp = v_lds + (32 * kb + 16 * h) * CPR * 16 + (vt_x ^ (uint32_t)(64 * db));
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
-    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * CPR * 16));
-    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
-    return u32x4{lo2[0], lo2[1], up2[0], up2[1]};
-  };
-  u32x4 vq[PFV];
-#pragma unroll
-  for (int i = 0; i < PFV; ++i)
-    if (i < NS2) vq[i] = v_read(i);
-#pragma unroll
-  for (int st = 0; st < NS2; ++st) {
-    const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
-    const u32x4 a = vq[st % PFV];
-    if (st + PFV < NS2) vq[st % PFV] = v_read(st + PFV);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = E::mfma(a, pb[rb][kb][h], acc_o[rb][db]);
-  }
-}
-
-template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int Sq, int Sk, int n_split, int chunk_keys, float c /* scale * log2(e) */) {
-  using ST = SplitTile<D>;
-  constexpr int RB = 1, Bc = ST::kBc, NKB = Bc / 32;
-  constexpr int CPR = D / 8, TB = ST::kTileBytes, LPW = ST::kLoadsPerWave;
-  constexpr int NDS = D / 16, NDB = D / 32;
-
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[ST::kLdsBytes];
-  constexpr uint32_t kK0 = 0, kK1 = TB, kV0 = 2 * TB, kV1 = 3 * TB;
-  static_assert((TB & (TB - 1)) == 0, "stage ^ TB toggles between the two stages of a ring");
-
-  const int lane = threadIdx.x & 63;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int split = blockIdx.x % n_split;
-  const int qblk = blockIdx.x / n_split;
-  const int bh = blockIdx.y + gridDim.y * blockIdx.z;
-  const int q0 = qblk * 32;
-  const int row = q0 + l32;
-  const int off = Sk - Sq;  // position of query 0 in the sequence
-
-  // this chunk's keys, cut short where no row of the block can see them
-  const int k_begin = split * chunk_keys;
-  int k_end = min(k_begin + chunk_keys, Sk);
-  if (CAUSAL) k_end = min(k_end, min(q0 + 31, Sq - 1) + off + 1);
-  // keys this lane's row keeps, within the chunk
-  const int row_lim = CAUSAL ? min(k_end, row + off + 1) : k_end;
-
-  u32x4 qf[RB][NDS];
-#pragma unroll
-  for (int s = 0; s < NDS; ++s) {
-    qf[0][s] = u32x4{0, 0, 0, 0};
-    if (row < Sq) qf[0][s] = *(const u32x4*)(q + ((size_t)bh * Sq + row) * D + 16 * s + 8 * hi);
-  }
-
-  const uint32_t head_bytes = (uint32_t)Sk * D * 2;
-  const unsigned char* k_head = (const unsigned char*)(k + (size_t)bh * Sk * D);
-  const unsigned char* v_head = (const unsigned char*)(v + (size_t)bh * Sk * D);
-  uint32_t k_off[LPW], v_off[LPW];
-  tile_load_offsets<D, LPW, false>(0, lane, k_off);
-  tile_load_offsets<D, LPW, true>(0, lane, v_off);
-  const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ swz_k<D>(l32)));
-  const int vt_row = 4 * hi + (lane & 15) / 4;
-  const int vt_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const uint32_t vt_x = (uint32_t)((vt_row * CPR + vt_chunk) * 16 + 8 * (lane & 1) +
-                                   64 * (swz_v<D>(vt_row) >> 2));
-
-  f32x16 acc_o[RB][NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc_o[0][db] = f32x16{};
-  float m_run[RB] = {-INFINITY}, l_run[RB] = {0.f}, l_rnd[RB] = {0.f};
-  const float one[RB] = {1.f};
-
-  const int t_first = k_begin / Bc;
-  const int n_t = k_end > k_begin ? (k_end - k_begin + Bc - 1) / Bc : 0;
-  if (n_t > 0) {
-    load_tile<LPW, TB>(k_head, head_bytes, t_first, smem + kK0, 0, k_off);
-    load_tile<LPW, TB>(v_head, head_bytes, t_first, smem + kV0, 0, v_off);
-  }
-  for (int t = 0; t < n_t; ++t) {
-    const uint32_t ks = (t & 1) ? kK1 : kK0, vs = (t & 1) ? kV1 : kV0;
-    // tile t has landed, and every LDS read of tile t - 1 is done, so its
-    // stages can take tile t + 1
-    wait_vm_lgkm0<0>();
-    if (t + 1 < n_t) {
-      load_tile<LPW, TB>(k_head, head_bytes, t_first + t + 1, smem + (ks ^ TB), 0, k_off);
-      load_tile<LPW, TB>(v_head, head_bytes, t_first + t + 1, smem + (vs ^ TB), 0, v_off);
-    }
-    f32x16 sc[RB][NKB];
-    tile_scores<D, DT, RB, NKB>(smem, ks, k_lane, qf, sc);
-    tile_mask_lim<NKB>(sc, (t_first + t) * Bc, row_lim, c, hi);
-    float tm[RB];
-    tile_max<RB, NKB>(sc, one, tm);
-    // exact running max; a row with no key so far keeps m = -inf and uses 0
-    // as its exponent reference
-    const float m_new = fmaxf(m_run[0], tm[0]);
-    const float m_ref[RB] = {m_new == -INFINITY ? 0.f : m_new};
-    const float alpha = m_run[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[0] - m_ref[0]);
-    l_run[0] *= alpha;
-    l_rnd[0] *= alpha;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc_o[0][db] *= alpha;
-    m_run[0] = m_new;
-    float tsum[RB], trnd[RB];
-    u32x4 pb[RB][NKB][2];
-    tile_probs<DT, RB, NKB>(sc, one, m_ref, tsum, trnd, pb);
-    l_run[0] += tsum[0];
-    l_rnd[0] += trnd[0];
-    tile_pv<D, DT, RB, NKB>(smem, vs, vt_x, pb, acc_o);
-  }
-
-  // partial state of rows < Sq
-  const float lr = xor32_sum(l_run[0]), lo = xor32_sum(l_rnd[0]);
-  if (row < Sq) {
-    const size_t prow = ((size_t)bh * n_split + split) * Sq + row;
-    float* po = part_o + prow * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 val = {acc_o[0][db][4 * g], acc_o[0][db][4 * g + 1], acc_o[0][db][4 * g + 2],
-                            acc_o[0][db][4 * g + 3]};
-        *(float4*)(po + 32 * db + 8 * g + 4 * hi) = val;
-      }
-    if (hi == 0) {
-      part_ml[prow * 3 + 0] = m_run[0];
-      part_ml[prow * 3 + 1] = lr;
-      part_ml[prow * 3 + 2] = lo;
-    }
-  }
-}
-
-// Merge the chunks of each query row: one wave per row, D / 64 columns per
-// lane.
-template <int D, int DT>
-__global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int n_rows, int Sq, int n_split) {
-  using E = Elem<DT>;
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= n_rows) return;  // whole waves leave together
-  const int bh = r / Sq, i = r % Sq;
-  const size_t first = (size_t)bh * n_split * Sq + i;  // partial row of chunk 0
-  float mx = -INFINITY;
-  for (int g = 0; g < n_split; ++g) {
-    const float* ml = part_ml + (first + (size_t)g * Sq) * 3;
-    if (ml[2] > 0.f) mx = fmaxf(mx, ml[0]);
-  }
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  float den = 0.f, lsum = 0.f;
-  for (int g = 0; g < n_split; ++g) {
-    const size_t prow = first + (size_t)g * Sq;
-    const float* ml = part_ml + prow * 3;
-    const float w = ml[2] > 0.f ? __builtin_amdgcn_exp2f(ml[0] - mx) : 0.f;
-    lsum += w * ml[1];
-    den += w * ml[2];
-    const float* po = part_o + prow * D;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += w * po[lane * PER + e];
-  }
-  const float inv = 1.0f / den;
-  uint16_t* orow = o + (size_t)r * D;
-#pragma unroll
-  for (int e = 0; e < PER; e += 2) {
-    const uint32_t pk = E::pack2(num[e] * inv, (e + 1 < PER ? num[e + 1] : 0.f) * inv);
-    if (PER >= 2) {
-      *(uint32_t*)(orow + lane * PER + e) = pk;
-    } else {
-      orow[lane] = (uint16_t)(pk & 0xffffu);
-    }
-  }
-  if (lane == 0) lse[r] = (mx + __builtin_amdgcn_logf(lsum)) * kLn2;
-}
-
-// Key chunks per (b, h) for a launch: enough workgroups for about two on
-// every compute unit (decoding is bandwidth bound; each one-wave workgroup
-// keeps a K and a V tile in flight), each chunk at least 4 tiles long.
-int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu) {
-  const long long n_qblk = (Sq + 31) / 32;
-  const long long n_tiles = (Sk + SplitTile<64>::kBc - 1) / SplitTile<64>::kBc;
-  // measured on decode shapes: more, shorter chunks lose bandwidth
-  const long long target = 2LL * n_cu;
-  long long want = (target + (long long)B * H * n_qblk - 1) / ((long long)B * H * n_qblk);
-  const long long cap = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  if (want > 1024) want = 1024;
-  return (int)want;
-}
-
-template <int D, int DT, bool CAUSAL>
-hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                          int H, int Sq, int Sk, float scale, int n_split, void* ws,
-                          hipStream_t stream) {
-  using ST = SplitTile<D>;
-  // chunks of whole tiles; trailing splits that would be empty are dropped
-  const int n_tiles = (Sk + ST::kBc - 1) / ST::kBc;
-  const int chunk_tiles = (n_tiles + n_split - 1) / n_split;
-  const int n_eff = (n_tiles + chunk_tiles - 1) / chunk_tiles;
-  const int n_qblk = (Sq + 31) / 32;
-  float* part_o = (float*)ws;
-  float* part_ml = (float*)((char*)ws + splitkv_part_o_bytes(B, H, Sq, D, n_eff));
-  const dim3 grid((unsigned)(n_eff * n_qblk), (unsigned)H, (unsigned)B);
-  fa2_splitkv_partial_kernel<D, DT, CAUSAL><<<grid, dim3(64), 0, stream>>>(
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, part_o, part_ml, Sq, Sk, n_eff,
-      chunk_tiles * ST::kBc, scale * kLog2e);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const int n_rows = B * H * Sq;
-  fa2_splitkv_combine_kernel<D, DT><<<dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
-      part_o, part_ml, (uint16_t*)o, lse, n_rows, Sq, n_eff);
-  return hipGetLastError();
-}
-
-template <int D, int DT>
-hipError_t launch_splitkv_causal(int causal, const void* q, const void* k, const void* v, void* o,
-                                 float* lse, int B, int H, int Sq, int Sk, float scale,
-                                 int n_split, void* ws, hipStream_t stream) {
-  return causal ? launch_splitkv<D, DT, true>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_split, ws, stream)
-                : launch_splitkv<D, DT, false>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_split, ws, stream);
-}
-
-template <int D>
-hipError_t launch_splitkv_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
-                                void* o, float* lse, int B, int H, int Sq, int Sk, float scale,
-                                int n_split, void* ws, hipStream_t stream) {
-  return dtype == FA2_F16 ? launch_splitkv_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, Sq, Sk,
-                                                               scale, n_split, ws, stream)
-                          : launch_splitkv_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, Sq,
-                                                                Sk, scale, n_split, ws, stream);
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + nb && b0 < a0 + na;
-}
-
-// Per-device verdict on whether the device is gfx950 (0 unknown, 1 yes,
-// 2 no) and its compute-unit count, both cached on first use.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_device_ok[kMaxDevices];
-std::atomic<int> g_device_cus[kMaxDevices];
-
-int check_device(int* n_cu) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return FA2_ERR_NO_DEVICE;
-  }
-  int verdict = g_device_ok[dev].load(std::memory_order_acquire);
-  if (verdict == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
-      (void)hipGetLastError();
-      return FA2_ERR_NO_DEVICE;
-    }
-    verdict = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    g_device_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
-                            std::memory_order_relaxed);
-    g_device_ok[dev].store(verdict, std::memory_order_release);
-  }
-  *n_cu = g_device_cus[dev].load(std::memory_order_relaxed);
-  return verdict == 1 ? FA2_OK : FA2_ERR_NO_DEVICE;
-}
-
 }  // namespace
-
-extern "C" int fa2_supported(int D, int dtype) {
-  return (D == 64 || D == 128 || D == 256) && (dtype == FA2_F16 || dtype == FA2_BF16);
-}
 
 extern "C" int fa2_rows_per_workgroup(int D) {
   switch (D) {
@@ -1118,26 +532,6 @@ extern "C" int fa2_rows_per_workgroup(int D) {
     case 128: return Shape<128>::kBr;
     case 256: return Shape<256>::kBr;
     default: return 0;
-  }
-}
-
-extern "C" const char* fa2_status_string(int status) {
-  switch (status) {
-    case FA2_OK: return "ok";
-    case FA2_ERR_NULL: return "a tensor pointer is NULL";
-    case FA2_ERR_SHAPE:
-      return "B, H and S must be >= 1, B and H <= 65535, one head (S*D elements) under 2 GiB, "
-             "and the grid within 2^31 workgroups";
-    case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
-    case FA2_ERR_DTYPE: return "dtype must be FA2_F16 or FA2_BF16";
-    case FA2_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";
-    case FA2_ERR_SCALE: return "scale must be finite and >= 0";
-    case FA2_ERR_NO_DEVICE: return "no current HIP device, or it is not a gfx950 (MI355X)";
-    case FA2_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
-    case FA2_ERR_ALIAS: return "o or lse overlaps q, k, v or each other (or the workspace overlaps any of them)";
-    case FA2_ERR_WORKSPACE:
-      return "the workspace is NULL, not 16-byte aligned, or smaller than fa2_splitkv_workspace_bytes";
-    default: return "unknown fa2 status";
   }
 }
 
@@ -1181,84 +575,6 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, flo
       break;
     default:
       err = launch_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st);
-      break;
-  }
-  return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
-}
-
-extern "C" int fa2_splitkv_splits(int B, int H, int Sq, int Sk) {
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return 1;
-  int n_cu = 0;
-  if (check_device(&n_cu) != FA2_OK) n_cu = 256;
-  return splitkv_default_splits(B, H, Sq, Sk, n_cu);
-}
-
-extern "C" size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int n_split) {
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || n_split < 0) return 0;
-  if (!(D == 64 || D == 128 || D == 256)) return 0;
-  if (n_split == 0) n_split = fa2_splitkv_splits(B, H, Sq, Sk);
-  return splitkv_workspace_bytes(B, H, Sq, D, n_split);
-}
-
-extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int Sq, int Sk, int D, int causal, float scale,
-                               int dtype, int n_split, void* workspace, size_t workspace_bytes,
-                               void* stream) {
-  if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || B > 65535 || H > 65535 || n_split < 0)
-    return FA2_ERR_SHAPE;
-  if (causal && Sq > Sk) return FA2_ERR_SHAPE;  // the first queries would have no key
-  if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
-  if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
-  // one head of K or V, plus a tile past its end, within 32-bit byte offsets;
-  // query rows of the whole call indexed in 32 bits
-  if (((long long)Sk + 256) * D * 2 > (long long)INT32_MAX) return FA2_ERR_SHAPE;
-  if ((long long)B * H * Sq > (long long)INT32_MAX / 4) return FA2_ERR_SHAPE;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
-  if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
-  // the default split count needs the device's size; an explicit one lets
-  // every argument be checked before the device is looked up
-  int n_cu = 0;
-  bool device_checked = false;
-  if (n_split == 0) {
-    const int dev = check_device(&n_cu);
-    if (dev != FA2_OK) return dev;
-    device_checked = true;
-    n_split = splitkv_default_splits(B, H, Sq, Sk, n_cu);
-  }
-  if (n_split > 65536) return FA2_ERR_SHAPE;
-  const size_t need = splitkv_workspace_bytes(B, H, Sq, D, n_split);
-  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return FA2_ERR_WORKSPACE;
-  const size_t q_bytes = (size_t)B * H * Sq * D * 2, kv_bytes = (size_t)B * H * Sk * D * 2;
-  const size_t lse_bytes = (size_t)B * H * Sq * sizeof(float);
-  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
-      overlaps(o, q_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, q_bytes) ||
-      overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
-      overlaps(lse, lse_bytes, o, q_bytes) || overlaps(workspace, need, q, q_bytes) ||
-      overlaps(workspace, need, k, kv_bytes) || overlaps(workspace, need, v, kv_bytes) ||
-      overlaps(workspace, need, o, q_bytes) || overlaps(workspace, need, lse, lse_bytes))
-    return FA2_ERR_ALIAS;
-  if (!device_checked) {
-    const int dev = check_device(&n_cu);
-    if (dev != FA2_OK) return dev;
-  }
-
-  (void)hipGetLastError();
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t err;
-  switch (D) {
-    case 64:
-      err = launch_splitkv_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, n_split,
-                                     workspace, st);
-      break;
-    case 128:
-      err = launch_splitkv_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, n_split,
-                                      workspace, st);
-      break;
-    default:
-      err = launch_splitkv_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, n_split,
-                                      workspace, st);
       break;
   }
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;

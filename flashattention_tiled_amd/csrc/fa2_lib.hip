@@ -1,0 +1,6 @@
+// The library is compiled as one translation unit from its parts: the
+// host-side runtime pieces, the prefill kernel with fa2_fwd, and the split-KV
+// decoding kernels with fa2_fwd_splitkv.
+#include "fa2_runtime.hip"
+#include "fa2_fwd.hip"
+#include "fa2_splitkv.hip"

@@ -40,6 +40,59 @@ def test_library_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def _elf_dynamic(path):
+    """(NEEDED libraries, defined global function names) of a shared object,
+    read with binutils."""
+    import subprocess
+
+    dyn = subprocess.run(["readelf", "-d", path], capture_output=True, text=True,
+                         check=True).stdout
+    needed = re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", dyn)
+    syms = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                          check=True).stdout
+    defined = [ln.split()[-1] for ln in syms.splitlines() if re.match(r"^\S+ T ", ln)]
+    return needed, defined
+
+
+def test_library_exports_only_the_declared_functions(lib):
+    _, defined = _elf_dynamic(fa.LIB_PATH)
+    ours = sorted(n for n in defined if n.startswith("fa2"))
+    assert ours == sorted(_declared_functions())
+    # internal helpers stay hidden
+    assert not [n for n in defined if "check_device" in n or "overlaps" in n]
+
+
+def test_product_path_is_independent_of_the_oracle(lib):
+    # the HIP library links no oracle code and its sources include none
+    needed, defined = _elf_dynamic(fa.LIB_PATH)
+    assert not [n for n in needed if "oracle" in n]
+    assert not [n for n in defined if "oracle" in n]
+    csrc = os.path.join(ROOT, "flashattention_tiled_amd", "csrc")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        assert "oracle" not in text, name
+    # the Python binding neither imports nor names the oracle package
+    pkg = os.path.join(ROOT, "flashattention_tiled_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            text = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), name
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library first thing in a process (as a test module's
+    collection can) still maps one HIP runtime, torch's: the device pointers
+    and streams the library is given come from torch's."""
+    import subprocess
+    import sys
+
+    code = ("import flashattention_tiled_amd as fa; fa.load_library(); "
+            "print('\\n'.join(fa._hip_runtimes_mapped()))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True,
+                         text=True, check=True).stdout.split()
+    assert len(out) == 1 and "torch" in out[0], out
+
+
 def test_enums_match_header():
     text = open(HEADER).read()
     for name, value in re.findall(r"(FA2_\w+)\s*=\s*(\d+)", text):
