@@ -8,6 +8,7 @@ Prints one JSON line on stdout; diagnostics go to stderr.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --table PATH      # every benchmark shape, one line each
     python bench.py --decode-table PATH   # split-KV decode shapes, GB/s
+    python bench.py --layer           # attention layer it/s and peak memory
 
 Metric: TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal masking, and the
 fraction of the MI355X dense fp16/bf16 matrix-core peak (256 CUs x 2.4 GHz x
@@ -182,6 +183,83 @@ def run_decode_table(path: str, steps: int):
         f.write("\n".join(rows) + "\n")
 
 
+def run_layer_bench(steps: int):
+    """The attention-layer measurements of the cookbook notebook ("FlashAttention-2
+    in an attention layer": "Memory growth", "Throughput"): FA2Attention's
+    forward passes per second at B=1, T=2048 for its prose shape (32 heads of
+    128) and its code shape (16 heads of 64), against a layer that stores the
+    T x T scores as SDPA's math backend does (same weights; its products are
+    contiguous fp16 matmuls), and the peak allocation of each at T=512 and
+    T=2048. Prints one JSON line per shape."""
+    import torch
+    from torch import nn
+
+    from flashattention_tiled_amd.layer import FA2Attention
+
+    class ScoresAttention(nn.Module):
+        """The baseline: scores materialised, fp32 softmax, causal."""
+
+        def __init__(self, ref: FA2Attention):
+            super().__init__()
+            self.qkv, self.o, self.h, self.d = ref.qkv, ref.o, ref.num_heads, ref.head_dim
+
+        def forward(self, x):
+            B, T, _ = x.shape
+            qkv = self.qkv(x).view(B, T, 3, self.h, self.d)
+            q, k, v = (qkv[:, :, i].transpose(1, 2).contiguous() for i in range(3))
+            s = torch.matmul(q, k.transpose(-1, -2).contiguous()).float() / math.sqrt(self.d)
+            mask = torch.ones((T, T), dtype=torch.bool, device=x.device).triu_(1)
+            p = torch.softmax(s.masked_fill_(mask, float("-inf")), dim=-1).to(x.dtype)
+            out = torch.matmul(p, v)
+            return self.o(out.transpose(1, 2).reshape(B, T, -1))
+
+    dev = torch.device("cuda:0")
+
+    def its(layer, x):
+        with torch.inference_mode():
+            for _ in range(5):
+                layer(x)
+            torch.cuda.synchronize(dev)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                layer(x)
+            torch.cuda.synchronize(dev)
+        return steps / (time.perf_counter() - t0)
+
+    def peak_mib(layer, T, d_model):
+        torch.cuda.synchronize(dev)
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        x = torch.randn((1, T, d_model), device=dev, dtype=torch.float16)
+        with torch.inference_mode():
+            layer(x)
+        torch.cuda.synchronize(dev)
+        return torch.cuda.max_memory_allocated(dev) / 2 ** 20
+
+    for d_model, heads in ((4096, 32), (1024, 16)):
+        torch.manual_seed(0)
+        fa2 = FA2Attention(d_model, heads).to(device=dev, dtype=torch.float16)
+        ref = ScoresAttention(fa2)
+        x = torch.randn((1, 2048, d_model), device=dev, dtype=torch.float16)
+        # warm the clock up on the heavier layer first
+        t_w = time.perf_counter()
+        with torch.inference_mode():
+            while time.perf_counter() - t_w < 0.5:
+                ref(x)
+            torch.cuda.synchronize(dev)
+        r_fa2, r_ref = its(fa2, x), its(ref, x)
+        mem = {name: {T: peak_mib(m, T, d_model) for T in (512, 2048)}
+               for name, m in (("fa2", fa2), ("scores", ref))}
+        print(json.dumps({
+            "workload": f"layer_b1_t2048_d{d_model}_h{heads}_f16_causal",
+            "fa2_it_per_s": round(r_fa2, 1), "scores_it_per_s": round(r_ref, 1),
+            "speedup": round(r_fa2 / r_ref, 2),
+            "peak_mib": {n: {str(T): round(v, 1) for T, v in m.items()} for n, m in mem.items()},
+            "memory_growth_t512_to_t2048": {n: round(m[2048] / m[512], 2) for n, m in mem.items()},
+        }), flush=True)
+        del fa2, ref, x
+
+
 def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
     """Time the fp64 oracle on a random sample of rows of the same workload
     (about `budget_s` of CPU work) and compare those rows with the GPU output."""
@@ -273,6 +351,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--table", default=None, help="time every benchmark shape into a CSV")
+    ap.add_argument("--layer", action="store_true",
+                    help="time the attention layer against a score-materialising layer")
     ap.add_argument("--decode-table", default=None,
                     help="time the split-KV path on every decode shape into a CSV")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -295,6 +375,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.layer:
+        run_layer_bench(args.steps)
+        return
     if args.decode_table:
         run_decode_table(args.decode_table, args.steps)
         return

@@ -8,6 +8,8 @@ binding's functions raises.
 
 C entry points, re-exported under the same names:
     fa2_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, stream) -> int
+    fa2_fwd_strided(q, k, v, o, lse, B, H, S, D, strides, causal, scale, dtype,
+                    stream) -> int   (strides: 12 element strides)
     fa2_supported(D, dtype) -> int
     fa2_status_string(status) -> str
     fa2_rows_per_workgroup(D) -> int
@@ -15,7 +17,8 @@ C entry points, re-exported under the same names:
                     n_split, workspace, workspace_bytes, stream) -> int
     fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) -> int
     fa2_splitkv_splits(B, H, Sq, Sk) -> int
-plus the tensor-level conveniences ``attention(q, k, v, causal, scale)`` and
+plus the tensor-level conveniences ``attention(q, k, v, causal, scale)`` (any
+layout whose head dim is contiguous) and
 ``attention_splitkv(q, k, v, causal, scale, n_split)`` (Sq queries against Sk
 cached keys).
 """
@@ -44,9 +47,11 @@ FA2_ERR_NO_DEVICE = 7
 FA2_ERR_LAUNCH = 8
 FA2_ERR_ALIAS = 9
 FA2_ERR_WORKSPACE = 10
+FA2_ERR_STRIDE = 11
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_supported", "fa2_status_string", "fa2_rows_per_workgroup",
-                    "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits")
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_supported", "fa2_status_string",
+                    "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
+                    "fa2_splitkv_splits")
 
 
 class FA2Error(RuntimeError):
@@ -96,6 +101,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa2_fwd.restype = i
+    lib.fa2_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i,
+                                    ctypes.POINTER(ctypes.c_longlong), i, f, i, vp]
+    lib.fa2_fwd_strided.restype = i
     lib.fa2_supported.argtypes = [i, i]
     lib.fa2_supported.restype = i
     lib.fa2_status_string.argtypes = [i]
@@ -118,6 +126,15 @@ def fa2_fwd(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D:
     """Direct call of the C entry point with raw device addresses; returns the status."""
     return int(load_library().fa2_fwd(q, k, v, o, lse, B, H, S, D, int(causal),
                                       float(scale), int(dtype), stream))
+
+
+def fa2_fwd_strided(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+                    strides, causal: int, scale: float, dtype: int, stream: int) -> int:
+    """Direct call of the strided entry point; `strides` is a sequence of 12
+    element strides (batch, head, seq of q, k, v, o). Returns the status."""
+    st = None if strides is None else (ctypes.c_longlong * 12)(*[int(x) for x in strides])
+    return int(load_library().fa2_fwd_strided(q, k, v, o, lse, B, H, S, D, st, int(causal),
+                                              float(scale), int(dtype), stream))
 
 
 def fa2_supported(D: int, dtype: int) -> int:
@@ -163,11 +180,15 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
               stream=None):
     """O, lse = softmax(scale * q k^T [causal]) v for (B, H, S, D) CUDA tensors.
 
-    q, k, v: contiguous torch tensors on one GPU, fp16 or bf16, same shape.
-    scale defaults to 1/sqrt(D). Returns (o, lse): o like q, lse (B, H, S)
-    float32 (natural-log logsumexp per row). `out`/`lse` may be passed
-    preallocated. Runs on `stream` (default: torch's current stream) without
-    synchronising. Raises FA2Error on any nonzero status.
+    q, k, v: torch tensors on one GPU, fp16 or bf16, same shape, each with a
+    contiguous last (head) dim; other strides are free (e.g. the (B, H, S, D)
+    views of a packed (B, S, 3, H, D) projection). Contiguous tensors go to
+    fa2_fwd, others to fa2_fwd_strided. scale defaults to 1/sqrt(D). Returns
+    (o, lse): o of q's shape (a new contiguous tensor unless `out`, which may
+    be any view with a contiguous last dim, is given), lse (B, H, S) float32
+    (natural-log logsumexp per row). Runs on `stream` (default: torch's
+    current stream) without synchronising. Raises FA2Error on any nonzero
+    status.
     """
     import torch
 
@@ -178,25 +199,32 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         raise ValueError("q, k and v must have one dtype")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k and v must be contiguous (B, H, S, D)")
+    if not (q.stride(3) == 1 and k.stride(3) == 1 and v.stride(3) == 1):
+        raise ValueError("q, k and v must have a contiguous last (head) dim")
     B, H, S, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(3) != 1:
+        raise ValueError("out must be a tensor of q's shape and dtype with a contiguous last dim")
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, H, S) tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    contiguous = all(t.is_contiguous() for t in (q, k, v, out))
     with torch.cuda.device(q.device):
-        status = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                         lse.data_ptr(), B, H, S, D, int(bool(causal)), float(scale),
-                         _dtype_code(q), stream.cuda_stream)
+        if contiguous:
+            status = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, S, D, int(bool(causal)), float(scale),
+                             _dtype_code(q), stream.cuda_stream)
+        else:
+            strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
+            status = fa2_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, S, D, strides, int(bool(causal)),
+                                     float(scale), _dtype_code(q), stream.cuda_stream)
     if status != FA2_OK:
         raise FA2Error(status, fa2_status_string(status))
     return out, lse

@@ -302,11 +302,18 @@ __device__ __forceinline__ void pipeline_block(
   }
 }
 
-template <int D, int DT, bool CAUSAL>
+// Element strides of the batch, head and sequence dims of Q, K, V and O (the
+// head dim is contiguous). Read only by the STRIDED kernels; the others use
+// the contiguous (B, H, S, D) layout.
+struct Strides {
+  long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
+};
+
+template <int D, int DT, bool CAUSAL, bool STRIDED>
 __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, float c /* scale * log2(e) */, int pair_split) {
+    int S, float c /* scale * log2(e) */, int pair_split, Strides st) {
   using SH = Shape<D>;
   using E = Elem<DT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
@@ -339,8 +346,28 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
   const int qt = (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh
                                                        : n_qt - 1 - lin / n_bh;
   const int q0 = qt * Br;
-  const size_t head = (size_t)bh * (size_t)S * D;
   const int wave_row0 = q0 + wave * SH::kRowsPerWave;
+
+  // This (b, h)'s Q, K, V and O, as element offsets from the base pointers,
+  // their row strides in elements, and K's and V's row strides in bytes.
+  size_t q_at, k_at, v_at, o_at, q_rs, o_rs;
+  uint32_t k_rb, v_rb;
+  if constexpr (STRIDED) {
+    const int b = bh / (int)gridDim.y, h = bh - b * (int)gridDim.y;
+    q_at = (size_t)(b * st.qb + h * st.qh);
+    k_at = (size_t)(b * st.kb + h * st.kh);
+    v_at = (size_t)(b * st.vb + h * st.vh);
+    o_at = (size_t)(b * st.ob + h * st.oh);
+    q_rs = (size_t)st.qs;
+    o_rs = (size_t)st.os;
+    k_rb = (uint32_t)st.ks * 2u;
+    v_rb = (uint32_t)st.vs * 2u;
+  } else {
+    const size_t head = (size_t)bh * (size_t)S * D;
+    q_at = k_at = v_at = o_at = head;
+    q_rs = o_rs = D;
+    k_rb = v_rb = 2u * D;
+  }
 
   // Q^T operands: lane holds Q[row][16 s + 8 hi .. +7] of each of its rows.
   u32x4 qf[RB][NDS];
@@ -350,17 +377,33 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
       qf[rb][s] = u32x4{0, 0, 0, 0};
-      if (row < S) qf[rb][s] = *(const u32x4*)(q + head + (size_t)row * D + 16 * s + 8 * hi);
+      if (row < S) qf[rb][s] = *(const u32x4*)(q + q_at + (size_t)row * q_rs + 16 * s + 8 * hi);
     }
   }
 
-  // K and V of this head, loaded through bounds-checked buffers.
-  const uint32_t head_bytes = (uint32_t)S * D * 2;
-  const unsigned char* k_head = (const unsigned char*)(k + head);
-  const unsigned char* v_head = (const unsigned char*)(v + head);
+  // K and V of this head, loaded through bounds-checked buffers that end
+  // with row S - 1 (loads of rows >= S return zero).
+  const uint32_t k_bytes = (uint32_t)S * k_rb, v_bytes = (uint32_t)S * v_rb;
+  const unsigned char* k_head = (const unsigned char*)(k + k_at);
+  const unsigned char* v_head = (const unsigned char*)(v + v_at);
   uint32_t k_off[LPW], v_off[LPW];
-  tile_load_offsets<D, LPW, false>(wave, lane, k_off);
-  tile_load_offsets<D, LPW, true>(wave, lane, v_off);
+  if constexpr (STRIDED) {
+    tile_load_offsets_strided<D, LPW, false>(wave, lane, k_rb, k_off);
+    tile_load_offsets_strided<D, LPW, true>(wave, lane, v_rb, v_off);
+  } else {
+    tile_load_offsets<D, LPW, false>(wave, lane, k_off);
+    tile_load_offsets<D, LPW, true>(wave, lane, v_off);
+  }
+  // buffer for key tile t of K or V (limit 0: a tile that is not needed,
+  // whose loads return zero)
+  auto k_tile = [&](uint32_t limit, int t) {
+    if constexpr (STRIDED) return tile_rsrc_at(k_head, limit, (uint32_t)t * (uint32_t)Bc * k_rb);
+    else return tile_rsrc<TB>(k_head, limit, t);
+  };
+  auto v_tile = [&](uint32_t limit, int t) {
+    if constexpr (STRIDED) return tile_rsrc_at(v_head, limit, (uint32_t)t * (uint32_t)Bc * v_rb);
+    else return tile_rsrc<TB>(v_head, limit, t);
+  };
 
   // LDS read offsets that do not depend on the tile.
   // K^T operand: row 32 kb + l32, chunk (2 s + hi) ^ swz_k(l32).
@@ -405,9 +448,9 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
   // tile j) has landed, and after the barrier every wave is done with
   // iteration j - 1, so K of tile j + 2 goes into tile j's K stage and V of
   // tile j + 1 into tile j - 1's V stage.
-  load_tile<LPW, TB>(k_head, head_bytes, 0, smem + kK0, wave, k_off);
-  load_tile<LPW, TB>(v_head, head_bytes, 0, smem + kV0, wave, v_off);
-  if (n_tiles > 1) load_tile<LPW, TB>(k_head, head_bytes, 1, smem + kK1, wave, k_off);
+  load_tile_rsrc<LPW>(k_tile(k_bytes, 0), smem + kK0, wave, k_off);
+  load_tile_rsrc<LPW>(v_tile(v_bytes, 0), smem + kV0, wave, v_off);
+  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(k_bytes, 1), smem + kK1, wave, k_off);
 
   f32x16 s_a[RB][NKB], s_b[RB][NKB];
   float ce_a[RB], ce_b[RB];
@@ -436,8 +479,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
     // K of tile j + 2 and V of tile j + 1; a tile past the workgroup's last
     // gets a zero-length buffer, so its loads only write zeros to a free stage
     const StepLoads<LPW> ld{
-        tile_rsrc<TB>(k_head, j + 2 < n_tiles ? head_bytes : 0u, j + 2),
-        tile_rsrc<TB>(v_head, j + 1 < n_tiles ? head_bytes : 0u, j + 1),
+        k_tile(j + 2 < n_tiles ? k_bytes : 0u, j + 2),
+        v_tile(j + 1 < n_tiles ? v_bytes : 0u, j + 1),
         smem + k_free, smem + v_free, k_off, v_off, wave};
     if (j < n_act) {
       // scores of tile j + 1 || probabilities of tile j, then P V of tile j
@@ -481,16 +524,18 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
         for (int g = 0; g < 4; ++g) {
           const u32x2 out = {E::pack2(acc_o[rb][db][4 * g] * inv, acc_o[rb][db][4 * g + 1] * inv),
                              E::pack2(acc_o[rb][db][4 * g + 2] * inv, acc_o[rb][db][4 * g + 3] * inv)};
-          *(u32x2*)(o + head + (size_t)row * D + 32 * db + 8 * g + 4 * hi) = out;
+          *(u32x2*)(o + o_at + (size_t)row * o_rs + 32 * db + 8 * g + 4 * hi) = out;
         }
       if (hi == 0) lse[(size_t)bh * S + row] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
 }
 
+// Launch the kernel over (B, H, S); `st` gives the strides of a strided call
+// (nullptr: contiguous tensors).
 template <int D, int DT, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                  int H, int S, float scale, int n_cu, hipStream_t stream) {
+                  int H, int S, float scale, const Strides* st, int n_cu, hipStream_t stream) {
   using SH = Shape<D>;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
   const dim3 grid((unsigned)n_qt, (unsigned)H, (unsigned)B);
@@ -501,27 +546,74 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const long long n_wg = (long long)n_qt * H * B;
   const int pair_split =
       (CAUSAL && n_qt > 1 && n_wg <= slots) ? (int)(((n_qt + 1) / 2) * (long long)H * B) : 0;
-  fa2_fwd_kernel<D, DT, CAUSAL><<<grid, block, 0, stream>>>(
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
-      scale * kLog2e, pair_split);
+  if (st)
+    fa2_fwd_kernel<D, DT, CAUSAL, true><<<grid, block, 0, stream>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
+        scale * kLog2e, pair_split, *st);
+  else
+    fa2_fwd_kernel<D, DT, CAUSAL, false><<<grid, block, 0, stream>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
+        scale * kLog2e, pair_split, Strides{});
   return hipGetLastError();
 }
 
 template <int D, int DT>
 hipError_t launch_causal(int causal, const void* q, const void* k, const void* v, void* o,
-                         float* lse, int B, int H, int S, float scale, int n_cu,
-                         hipStream_t stream) {
-  return causal ? launch<D, DT, true>(q, k, v, o, lse, B, H, S, scale, n_cu, stream)
-                : launch<D, DT, false>(q, k, v, o, lse, B, H, S, scale, n_cu, stream);
+                         float* lse, int B, int H, int S, float scale, const Strides* st,
+                         int n_cu, hipStream_t stream) {
+  return causal ? launch<D, DT, true>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
+                : launch<D, DT, false>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
 }
 
 template <int D>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
-                        void* o, float* lse, int B, int H, int S, float scale, int n_cu,
-                        hipStream_t stream) {
+                        void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
+                        int n_cu, hipStream_t stream) {
   return dtype == FA2_F16
-             ? launch_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, S, scale, n_cu, stream)
-             : launch_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, S, scale, n_cu, stream);
+             ? launch_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
+             : launch_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
+                                          stream);
+}
+
+hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k, const void* v,
+                      void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
+                      int n_cu, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
+    case 128:
+      return launch_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
+    default:
+      return launch_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
+  }
+}
+
+// Whether the rows (b, h, s) of a (B, H, S, D) tensor with these element
+// strides (head dim contiguous) are pairwise disjoint: taking the dims of
+// size > 1 in ascending stride order, each stride must reach past the span
+// of the dims before it.
+bool rows_disjoint(int B, int H, int S, int D, long long sb, long long sh, long long ss) {
+  long long n[3] = {B, H, S}, st[3] = {sb, sh, ss};
+  for (int i = 1; i < 3; ++i)
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      const long long tn = n[j], ts = st[j];
+      n[j] = n[j - 1];
+      st[j] = st[j - 1];
+      n[j - 1] = tn;
+      st[j - 1] = ts;
+    }
+  long long span = D;
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] < 2) continue;
+    if (st[i] < span) return false;
+    span += st[i] * (n[i] - 1);
+  }
+  return true;
+}
+
+// Bytes from a tensor's base pointer to the end of its last element.
+size_t extent_bytes(int B, int H, int S, int D, long long sb, long long sh, long long ss) {
+  return (size_t)(((long long)(B - 1) * sb + (long long)(H - 1) * sh + (long long)(S - 1) * ss +
+                   D) * 2);
 }
 
 }  // namespace
@@ -566,16 +658,57 @@ extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, flo
   if (dev != FA2_OK) return dev;
 
   (void)hipGetLastError();  // start from a clean error state
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t err;
-  switch (D) {
-    case 64: err = launch_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st); break;
-    case 128:
-      err = launch_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st);
-      break;
-    default:
-      err = launch_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, S, scale, n_cu, st);
-      break;
+  const hipError_t err = launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale, nullptr,
+                                    n_cu, (hipStream_t)stream);
+  return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+extern "C" int fa2_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int S, int D, const long long* strides, int causal,
+                               float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !strides) return FA2_ERR_NULL;
+  if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535) return FA2_ERR_SHAPE;
+  if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
+  if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
+  // every stride in [0, 2^40], a multiple of 8 elements (16-byte rows), and
+  // each sequence stride at least D
+  for (int i = 0; i < 12; ++i) {
+    const long long x = strides[i];
+    if (x < 0 || x > (1LL << 40) || (x & 7)) return FA2_ERR_STRIDE;
+    if (i % 3 == 2 && x < D) return FA2_ERR_STRIDE;
   }
+  const Strides st{strides[0], strides[1], strides[2],  strides[3], strides[4],  strides[5],
+                   strides[6], strides[7], strides[8],  strides[9], strides[10], strides[11]};
+  // one head of K or V, plus a tile of rows past its end, within 32-bit byte
+  // offsets (buffer loads)
+  if (((long long)S + 256) * st.ks * 2 > (long long)INT32_MAX ||
+      ((long long)S + 256) * st.vs * 2 > (long long)INT32_MAX)
+    return FA2_ERR_SHAPE;
+  const int rows = fa2_rows_per_workgroup(D);
+  const unsigned long long blocks = (((unsigned long long)S + rows - 1) / rows) *
+                                    (unsigned long long)H * (unsigned long long)B;
+  if (blocks > (unsigned long long)INT32_MAX) return FA2_ERR_SHAPE;
+  // the output's rows must not share memory
+  if (!rows_disjoint(B, H, S, D, st.ob, st.oh, st.os)) return FA2_ERR_STRIDE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
+  if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
+  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
+  // overlap of the outputs with anything, by the byte ranges the tensors span
+  const size_t qe = extent_bytes(B, H, S, D, st.qb, st.qh, st.qs);
+  const size_t ke = extent_bytes(B, H, S, D, st.kb, st.kh, st.ks);
+  const size_t ve = extent_bytes(B, H, S, D, st.vb, st.vh, st.vs);
+  const size_t oe = extent_bytes(B, H, S, D, st.ob, st.oh, st.os);
+  const size_t lse_bytes = (size_t)B * H * S * sizeof(float);
+  if (overlaps(o, oe, q, qe) || overlaps(o, oe, k, ke) || overlaps(o, oe, v, ve) ||
+      overlaps(lse, lse_bytes, q, qe) || overlaps(lse, lse_bytes, k, ke) ||
+      overlaps(lse, lse_bytes, v, ve) || overlaps(lse, lse_bytes, o, oe))
+    return FA2_ERR_ALIAS;
+  int n_cu = 0;
+  const int dev = check_device(&n_cu);
+  if (dev != FA2_OK) return dev;
+
+  (void)hipGetLastError();
+  const hipError_t err = launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale, &st, n_cu,
+                                    (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }

@@ -68,6 +68,9 @@ extern "C" const char* fa2_status_string(int status) {
     case FA2_ERR_NO_DEVICE: return "no current HIP device, or it is not a gfx950 (MI355X)";
     case FA2_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
     case FA2_ERR_ALIAS: return "o or lse overlaps q, k, v or each other (or the workspace overlaps any of them)";
+    case FA2_ERR_STRIDE:
+      return "strides must be in [0, 2^40] and multiples of 8, sequence strides >= D, and o's "
+             "rows must not overlap";
     case FA2_ERR_WORKSPACE:
       return "the workspace is NULL, not 16-byte aligned, or smaller than fa2_splitkv_workspace_bytes";
     default: return "unknown fa2 status";

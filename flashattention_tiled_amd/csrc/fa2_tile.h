@@ -157,6 +157,22 @@ __device__ __forceinline__ void tile_load_offsets(int wave, int lane, uint32_t (
   }
 }
 
+// The same offsets for key rows `row_bytes` apart in memory (a strided K or
+// V; row_bytes >= 2 D). Only the source offsets change: the LDS layout is
+// that of tile_load_offsets.
+template <int D, int LPW, bool IS_V>
+__device__ __forceinline__ void tile_load_offsets_strided(int wave, int lane, uint32_t row_bytes,
+                                                          uint32_t (&off)[LPW]) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int p = (wave * LPW + i) * 64 + lane;
+    const int r = p / CPR, cp = p % CPR;
+    const int c = cp ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+    off[i] = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
+  }
+}
+
 // Buffer descriptor for tile t of a head (K or V), rebased on the tile. Its
 // record count ends at `limit` bytes from the head start (the end of the
 // head, so that loads past S return zero; 0 for a tile that is not needed,
@@ -169,6 +185,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned char*
   const uint32_t start = (uint32_t)t * TB;
   const uint32_t left = (uint32_t)wave_uniform((int)(limit - (start < limit ? start : limit)));
   return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + start), 0, (int)left, kBufferFlags);
+}
+
+// The same for a tile that starts `start` bytes after the head start (a
+// strided K or V, whose tiles are B_c rows x the row stride apart).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc_at(const unsigned char* head_base,
+                                                               uint32_t limit, uint32_t start) {
+  const uint32_t s0 = (uint32_t)wave_uniform((int)start);
+  const uint32_t left = (uint32_t)wave_uniform((int)(limit - (s0 < limit ? s0 : limit)));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + s0), 0, (int)left, kBufferFlags);
 }
 
 // Block i (of this wave's LPW) of a tile load into LDS at `dst`: 64 lanes x
@@ -186,6 +211,14 @@ __device__ __forceinline__ void load_tile(const unsigned char* head_base, uint32
                                           int t, unsigned char* dst, int wave,
                                           const uint32_t* off) {
   const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc<TB>(head_base, head_bytes, t);
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) load_block<LPW>(rsrc, dst, wave, off[i], i);
+}
+
+// Start loading a whole tile (this wave's LPW blocks) through `rsrc`.
+template <int LPW>
+__device__ __forceinline__ void load_tile_rsrc(__amdgpu_buffer_rsrc_t rsrc, unsigned char* dst,
+                                               int wave, const uint32_t* off) {
 #pragma unroll
   for (int i = 0; i < LPW; ++i) load_block<LPW>(rsrc, dst, wave, off[i], i);
 }

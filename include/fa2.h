@@ -54,7 +54,9 @@ typedef enum {
     FA2_ERR_LAUNCH = 8,    /* the HIP runtime reported an error at launch */
     FA2_ERR_ALIAS = 9,     /* o or lse overlaps q, k or v, or o overlaps lse (split-KV:
                               or the workspace overlaps any tensor) */
-    FA2_ERR_WORKSPACE = 10 /* split-KV: workspace NULL, misaligned or too small */
+    FA2_ERR_WORKSPACE = 10, /* split-KV: workspace NULL, misaligned or too small */
+    FA2_ERR_STRIDE = 11     /* strided: a stride negative, above 2^40 or not a multiple of 8,
+                               a sequence stride below D, or o's rows overlapping */
 } fa2_status;
 
 /*
@@ -90,6 +92,32 @@ typedef enum {
 int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
             int B, int H, int S, int D, int causal, float scale, int dtype,
             void *stream);
+
+/*
+ * fa2_fwd_strided -- fa2_fwd on tensors laid out with arbitrary strides,
+ * such as the (B, S, H, D) views of a packed QKV projection that an
+ * attention layer produces (the cookbook notebook's FA2Attention transposes
+ * and copies them to (B, H, S, D) before its kernel; this call reads and
+ * writes them in place).
+ *
+ * strides  host pointer to 12 element strides: the batch, head and sequence
+ *          strides of q, then of k, v and o, in that order. Element
+ *          (b, h, s, d) of q is at q[b*strides[0] + h*strides[1] +
+ *          s*strides[2] + d]; the head dim is contiguous. Each stride is in
+ *          [0, 2^40] and a multiple of 8 (16-byte rows); each sequence
+ *          stride is >= D. Batch and head strides may be 0 for q, k and v
+ *          (a K/V shared by all heads), but o's rows must be disjoint.
+ * lse      contiguous (B, H, S) floats, as for fa2_fwd.
+ * Other arguments, the result and the arithmetic are those of fa2_fwd, and
+ * for contiguous strides the result is bit-identical to it. One head of K
+ * and of V must span under 2 GiB: (S + 256) * sequence stride * 2 bytes.
+ * Overlap is judged on the byte range each tensor spans, so o and lse must
+ * not fall within q's, k's or v's span. Returns FA2_ERR_STRIDE for bad
+ * strides, otherwise the codes of fa2_fwd.
+ */
+int fa2_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int S, int D, const long long *strides, int causal,
+                    float scale, int dtype, void *stream);
 
 /* 1 when fa2_fwd has a kernel for head dimension D and dtype, else 0. */
 int fa2_supported(int D, int dtype);

@@ -111,7 +111,7 @@ def test_supported_and_rows(lib):
 
 
 def test_status_strings(lib):
-    for s in range(11):
+    for s in range(12):
         assert fa.fa2_status_string(s)
     assert fa.fa2_status_string(0) == "ok"
     assert "unknown" in fa.fa2_status_string(99)
@@ -185,6 +185,67 @@ def test_no_device_status_without_gpu(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; the fake pointers must not be launched on")
     assert _call() == fa.FA2_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# strided entry point: B=2, H=3, S=100, D=64
+# ---------------------------------------------------------------------------
+_B, _H, _S = 2, 3, 100
+_CONTIG = [_H * _S * 64, _S * 64, 64] * 4
+_BSHD = [_S * _H * 64, 64, _H * 64] * 4
+SQ, SK, SV, SO, SL = (0x40000000 + i * 0x1000000 for i in range(5))
+
+
+def _call_strided(**kw):
+    args = dict(q=SQ, k=SK, v=SV, o=SO, lse=SL, B=_B, H=_H, S=_S, D=64, strides=list(_CONTIG),
+                causal=0, scale=0.125, dtype=fa.FA2_F16, stream=None)
+    args.update(kw)
+    return fa.fa2_fwd_strided(**args)
+
+
+def _with(base, **idx):
+    out = list(base)
+    for name, val in idx.items():
+        out[int(name[1:])] = val
+    return out
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA2_ERR_NULL),
+    (dict(strides=None), fa.FA2_ERR_NULL),
+    (dict(S=0), fa.FA2_ERR_SHAPE),
+    (dict(D=96), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA2_ERR_DTYPE),
+    (dict(strides=_with(_CONTIG, s0=-8)), fa.FA2_ERR_STRIDE),          # negative
+    (dict(strides=_with(_CONTIG, s4=4)), fa.FA2_ERR_STRIDE),           # not 16-byte rows
+    (dict(strides=_with(_CONTIG, s5=32)), fa.FA2_ERR_STRIDE),          # k rows overlap (< D)
+    (dict(strides=_with(_CONTIG, s1=(1 << 40) + 8)), fa.FA2_ERR_STRIDE),
+    (dict(strides=_with(_CONTIG, s10=64)), fa.FA2_ERR_STRIDE),         # o heads share rows
+    (dict(strides=_with(_CONTIG, s9=0)), fa.FA2_ERR_STRIDE),           # o batch broadcast
+    (dict(strides=_with(_CONTIG, s11=64 + 8, s10=100 * 64)), fa.FA2_ERR_STRIDE),  # rows spill into next head
+    (dict(strides=_with(_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),      # a K head past 2 GiB
+    (dict(k=SK + 8), fa.FA2_ERR_ALIGN),
+    (dict(lse=SL + 2), fa.FA2_ERR_ALIGN),
+    (dict(scale=float("inf")), fa.FA2_ERR_SCALE),
+    (dict(o=SQ + 1024), fa.FA2_ERR_ALIAS),
+    (dict(lse=SV + 4096), fa.FA2_ERR_ALIAS),
+])
+def test_strided_validation_status(lib, kw, status):
+    assert _call_strided(**kw) == status
+
+
+@pytest.mark.parametrize("strides", [
+    _CONTIG, _BSHD,
+    _with(_CONTIG, s3=0, s4=0, s6=0, s7=0),          # one K/V shared by every (b, h)
+    _with(_BSHD, s9=_S * (_H * 64 + 64), s11=_H * 64 + 64),  # padded o rows
+], ids=["contiguous", "bshd", "kv_broadcast", "padded_o"])
+def test_strided_valid_layouts_reach_the_device_check(lib, strides):
+    """Valid layouts pass every check before the device lookup (no GPU here:
+    FA2_ERR_NO_DEVICE; skipped where a GPU exists, the pointers are fake)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call_strided(strides=strides) == fa.FA2_ERR_NO_DEVICE
 
 
 # ---------------------------------------------------------------------------
