@@ -47,36 +47,52 @@ using fa2_host::overlaps;
 namespace {
 
 constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile sum of P
-// Phase-1 k-steps between this wave's tile-load blocks (0: all at the start
-// of the step). Spacing them out helps D = 128 slightly; D = 64 and D = 256
-// run best with all loads up front.
-template <int D> struct LoadEvery { static constexpr int kValue = D == 128 ? 2 : 0; };
-
-// Tile shape per head dimension.
-//   kWaves      waves per workgroup (they share the LDS rings)
-//   kRowBlocks  32-row MFMA blocks per wave
-//   kBc         keys per tile
+// Tile configuration per head dimension:
+//   kWaves         waves per workgroup (they share the LDS rings)
+//   kRowBlocks     32-row MFMA blocks per wave
+//   kBc            keys per tile
 //   kWavesPerSimd  waves per SIMD the register budget is sized for
+//   kLoadEvery     phase-1 k-steps between this wave's tile-load blocks (0: all
+//                  at the start of the step)
 // K and V each have a two-stage LDS ring: iteration j reads K of tile j + 1
 // and V of tile j while K of tile j + 2 and V of tile j + 1 load.
-template <int D> struct Tile;
-template <> struct Tile<64> {
-  static constexpr int kWaves = 4, kRowBlocks = 1, kBc = 64, kWavesPerSimd = 2;
+// The defaults are the best of a sweep over these five values on the
+// benchmark shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides
+// one, as "waves, row blocks, keys, waves per SIMD, load spacing". D = 64 has
+// a second configuration for sequences of at least FA2_D64_LONG_S (the LONG
+// tile): 32-key tiles at four waves per SIMD, 2-4% faster there and up to
+// 20% slower on short sequences.
+template <int W, int RB, int BC, int WPS, int LE> struct TileCfg {
+  static constexpr int kWaves = W, kRowBlocks = RB, kBc = BC, kWavesPerSimd = WPS, kLoadEvery = LE;
 };
-template <> struct Tile<128> {
-  static constexpr int kWaves = 4, kRowBlocks = 1, kBc = 64, kWavesPerSimd = 2;
-};
-template <> struct Tile<256> {
-  static constexpr int kWaves = 4, kRowBlocks = 1, kBc = 32, kWavesPerSimd = 1;
-};
+#ifndef FA2_TILE_D64
+#define FA2_TILE_D64 4, 1, 64, 2, 1
+#endif
+#ifndef FA2_TILE_D64_LONG
+#define FA2_TILE_D64_LONG 4, 1, 32, 4, 0
+#endif
+#ifndef FA2_D64_LONG_S
+#define FA2_D64_LONG_S 8192
+#endif
+#ifndef FA2_TILE_D128
+#define FA2_TILE_D128 4, 1, 64, 2, 2
+#endif
+#ifndef FA2_TILE_D256
+#define FA2_TILE_D256 4, 1, 32, 1, 0
+#endif
+template <int D, bool LONG = false> struct Tile;
+template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};
+template <> struct Tile<64, true> : TileCfg<FA2_TILE_D64_LONG> {};
+template <> struct Tile<128> : TileCfg<FA2_TILE_D128> {};
+template <> struct Tile<256> : TileCfg<FA2_TILE_D256> {};
 
-template <int D> struct Shape {
-  static constexpr int kWaves = Tile<D>::kWaves;
+template <int D, bool LONG = false> struct Shape {
+  static constexpr int kWaves = Tile<D, LONG>::kWaves;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRB = Tile<D>::kRowBlocks;
+  static constexpr int kRB = Tile<D, LONG>::kRowBlocks;
   static constexpr int kRowsPerWave = 32 * kRB;
   static constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
-  static constexpr int kBc = Tile<D>::kBc;
+  static constexpr int kBc = Tile<D, LONG>::kBc;
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per key row
   static constexpr int kTileBytes = kBc * D * 2;     // one K or one V tile
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per K (or V) tile
@@ -309,12 +325,12 @@ struct Strides {
   long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
 };
 
-template <int D, int DT, bool CAUSAL, bool STRIDED>
-__global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa2_fwd_kernel(
+template <int D, int DT, bool CAUSAL, bool STRIDED, bool LONG>
+__global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesPerSimd)) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int S, float c /* scale * log2(e) */, int pair_split, Strides st) {
-  using SH = Shape<D>;
+  using SH = Shape<D, LONG>;
   using E = Elem<DT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
   constexpr int CPR = SH::kChunksPerRow, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
@@ -486,7 +502,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
       // scores of tile j + 1 || probabilities of tile j, then P V of tile j
       // (past the wave's last tile the scores come from a stale stage and are
       // never used)
-      pipeline_block<D, DT, RB, NKB, LPW, LoadEvery<D>::kValue>(
+      pipeline_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery>(
           ld, smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt, acc_o);
       if (j + 1 < n_act) {
         if (tile_needs_mask<RB, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S)) {
@@ -533,57 +549,59 @@ __global__ __launch_bounds__(Shape<D>::kThreads, Tile<D>::kWavesPerSimd) void fa
 
 // Launch the kernel over (B, H, S); `st` gives the strides of a strided call
 // (nullptr: contiguous tensors).
-template <int D, int DT, bool CAUSAL>
+template <int D, int DT, bool CAUSAL, bool LONG>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int S, float scale, const Strides* st, int n_cu, hipStream_t stream) {
-  using SH = Shape<D>;
+  using SH = Shape<D, LONG>;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
   const dim3 grid((unsigned)n_qt, (unsigned)H, (unsigned)B);
   const dim3 block(SH::kThreads);
   // workgroups resident per compute unit: the register budget allows
   // kWavesPerSimd waves per SIMD, i.e. that many 4-wave workgroups
-  const long long slots = (long long)n_cu * Tile<D>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long slots = (long long)n_cu * Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves;
   const long long n_wg = (long long)n_qt * H * B;
   const int pair_split =
       (CAUSAL && n_qt > 1 && n_wg <= slots) ? (int)(((n_qt + 1) / 2) * (long long)H * B) : 0;
   if (st)
-    fa2_fwd_kernel<D, DT, CAUSAL, true><<<grid, block, 0, stream>>>(
+    fa2_fwd_kernel<D, DT, CAUSAL, true, LONG><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
         scale * kLog2e, pair_split, *st);
   else
-    fa2_fwd_kernel<D, DT, CAUSAL, false><<<grid, block, 0, stream>>>(
+    fa2_fwd_kernel<D, DT, CAUSAL, false, LONG><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
         scale * kLog2e, pair_split, Strides{});
   return hipGetLastError();
 }
 
-template <int D, int DT>
-hipError_t launch_causal(int causal, const void* q, const void* k, const void* v, void* o,
-                         float* lse, int B, int H, int S, float scale, const Strides* st,
-                         int n_cu, hipStream_t stream) {
-  return causal ? launch<D, DT, true>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
-                : launch<D, DT, false>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
-}
-
-template <int D>
+template <int D, bool LONG>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                         void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
                         int n_cu, hipStream_t stream) {
-  return dtype == FA2_F16
-             ? launch_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
-             : launch_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
-                                          stream);
+  if (dtype == FA2_F16)
+    return causal ? launch<D, FA2_F16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
+                  : launch<D, FA2_F16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu,
+                                                    stream);
+  return causal ? launch<D, FA2_BF16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
+                : launch<D, FA2_BF16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu,
+                                                   stream);
 }
 
 hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k, const void* v,
                       void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
                       int n_cu, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
+    case 64:
+      return S >= FA2_D64_LONG_S
+                 ? launch_dtype<64, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
+                                          stream)
+                 : launch_dtype<64, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st,
+                                           n_cu, stream);
     case 128:
-      return launch_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
+      return launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
+                                      stream);
     default:
-      return launch_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu, stream);
+      return launch_dtype<256, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
+                                      stream);
   }
 }
 
@@ -617,6 +635,9 @@ size_t extent_bytes(int B, int H, int S, int D, long long sb, long long sh, long
 }
 
 }  // namespace
+
+static_assert(Shape<64, true>::kBr == Shape<64>::kBr,
+              "both D = 64 tiles take the query rows per workgroup fa2_rows_per_workgroup reports");
 
 extern "C" int fa2_rows_per_workgroup(int D) {
   switch (D) {

@@ -125,7 +125,7 @@ def test_scale_values():
 # ---------------------------------------------------------------------------
 # the benchmark shapes at full size, sampled rows
 # ---------------------------------------------------------------------------
-FULL = wl.SWEEP + wl.LLM_LAYER + [wl.LONG_PREFILL, wl.RAGGED_D256]
+FULL = wl.SWEEP + wl.LLM_LAYER + [wl.LONG_PREFILL, wl.RAGGED_D256, wl.ONE_GPU_SHARE]
 
 
 @pytest.mark.parametrize("w", FULL, ids=lambda w: w.name)
@@ -139,3 +139,29 @@ def test_full_size_sampled(w):
     o_s = o.reshape(-1, w.D)[torch.from_numpy(rows)]
     lse_s = lse.reshape(-1)[torch.from_numpy(rows)]
     assert_parity(o_s, lse_s, o_ref, lse_ref, w.dtype, f"{w.name} ({len(rows)} rows)")
+
+
+@pytest.mark.parametrize("S", [8192, 8223, 12001])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_d64_long_sequence_tile(S, dtype, causal):
+    """D = 64 switches to its long-sequence tile (32 keys, four waves per
+    SIMD) at S >= 8192: sampled rows, including the ragged tail, against the
+    oracle, and the peaky rising-score case that forces the lazy rescale."""
+    w = wl.Workload("d64_long", 1, 3, S, 64, dtype, causal)
+    announce(f"d64 long tile S={S} {dtype} causal={causal}")
+    q, k, v = wl.make_qkv(w, seed=S)
+    o, lse = run_gpu(q, k, v, causal, w.scale)
+    rows = sample_rows(w.B, w.H, S, seed=S, tile=128)
+    o_ref, lse_ref = oracle_rows(q, k, v, rows, causal, w.scale)
+    o_s = o.reshape(-1, 64)[torch.from_numpy(rows)]
+    lse_s = lse.reshape(-1)[torch.from_numpy(rows)]
+    assert_parity(o_s, lse_s, o_ref, lse_ref, dtype, f"d64 long S={S} ({len(rows)} rows)")
+    if S == 8223:
+        q2, k2, v2 = _ramp_inputs(S, 64, dtype, +1, seed=1)
+        o2, lse2 = run_gpu(q2, k2, v2, causal, w.scale)
+        rows2 = sample_rows(1, 2, S, seed=S + 1, tile=128)
+        o_ref2, lse_ref2 = oracle_rows(q2, k2, v2, rows2, causal, w.scale)
+        assert_parity(o2.reshape(-1, 64)[torch.from_numpy(rows2)],
+                      lse2.reshape(-1)[torch.from_numpy(rows2)], o_ref2, lse_ref2, dtype,
+                      f"d64 long rising scores S={S}")

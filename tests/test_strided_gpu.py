@@ -147,3 +147,18 @@ def test_strided_rejects_bad_strides():
     with pytest.raises(fa.FA2Error) as e:
         fa.attention(x, x, x, out=bad_out)  # every head's O in the same rows
     assert e.value.status == fa.FA2_ERR_STRIDE
+
+
+def test_strided_d64_long_sequence_tile():
+    """The D = 64 long-sequence tile (S >= 8192) on packed QKV views: bitwise
+    equal to the contiguous call."""
+    B, H, S, D = 1, 2, 8200, 64
+    announce("strided packed qkv d64 S=8200")
+    w = wl.Workload("strided", B, H, S, D, "bf16", True)
+    q, k, v = wl.make_qkv(w, seed=5)
+    views, _ = _strided("packed_qkv", q, k, v)
+    o_s, lse_s = fa.attention(*views, causal=True, scale=w.scale,
+                              out=_out_like("packed_qkv", B, H, S, D, q.dtype))
+    o_c, lse_c = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_c) and torch.equal(lse_s, lse_c)

@@ -163,7 +163,12 @@ LONG_PREFILL = Workload("long_prefill", 1, 8, 16384, 128, "bf16", False, qk_mult
 # Ragged large head dim: S = 4097 is not a tile multiple, D = 256, bf16 causal.
 RAGGED_D256 = Workload("ragged_d256", 4, 16, 4097, 256, "bf16", True)
 
-ALL = TINY + SWEEP + LLM_LAYER + [LONG_PREFILL, RAGGED_D256]
+# One GPU's share of the headline when its 32 (b, h) heads are split across 8
+# GPUs: 4 heads, 256 workgroups, about one per compute unit, which exposes
+# the causal tail imbalance.
+ONE_GPU_SHARE = Workload("share_b1_h4_s8192_d128", 1, 4, 8192, 128, "f16", True)
+
+ALL = TINY + SWEEP + LLM_LAYER + [LONG_PREFILL, RAGGED_D256, ONE_GPU_SHARE]
 
 TOLERANCE_O = {"f16": 2e-3, "bf16": 1.6e-2}
 TOLERANCE_LSE_REL = 1e-4
