@@ -130,21 +130,25 @@ def time_gpu_splitkv(w, steps: int, warmup_min_s: float):
     import workloads as wl
 
     dev = torch.device("cuda:0")
-    q, k, v = (x.to(dev) for x in wl.make_qkv_decode(w, seed=0))
+    kv8 = w.kv == "e4m3"
+    make = wl.make_qkv_decode_fp8 if kv8 else wl.make_qkv_decode
+    q, k, v = (x.to(dev) for x in make(w, seed=0))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.Sq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     lib = fa.load_library()
-    n_split = fa.fa2_splitkv_splits(w.B, w.H, w.Sq, w.Sk)
+    n_split = (fa.fa2_splitkv_splits_fp8 if kv8 else fa.fa2_splitkv_splits)(w.B, w.H, w.Sq, w.Sk)
     need = fa.fa2_splitkv_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, n_split)
     ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     dtype = fa.FA2_F16 if w.dtype == "f16" else fa.FA2_BF16
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            w.B, w.H, w.Sq, w.Sk, w.D, int(w.causal), float(w.scale), dtype, n_split,
-            ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.Sq, w.Sk, w.D, int(w.causal), float(w.scale))
+    tail = (dtype, n_split, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    entry = lib.fa2_fwd_splitkv_fp8 if kv8 else lib.fa2_fwd_splitkv
+    args = head + ((float(w.k_descale), float(w.v_descale)) if kv8 else ()) + tail
 
     def launch():
-        st = lib.fa2_fwd_splitkv(*args)
+        st = entry(*args)
         if st != 0:
             raise fa.FA2Error(st, fa.fa2_status_string(st))
 
@@ -167,18 +171,19 @@ def run_decode_table(path: str, steps: int):
     import workloads as wl
 
     rows = []
-    for w in wl.DECODE:
+    for w in wl.DECODE + wl.DECODE_FP8:
         n_split, durs = time_gpu_splitkv(w, steps, warmup_min_s=0.3)
         med = durs[len(durs) // 2]
         avg = sum(durs) / len(durs)
         gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9
-        line = (f"{w.name},{w.B},{w.H},{w.Sq},{w.Sk},{w.D},{w.dtype},{int(w.causal)},{n_split},"
+        line = (f"{w.name},{w.B},{w.H},{w.Sq},{w.Sk},{w.D},{w.dtype},{w.kv or w.dtype},"
+                f"{int(w.causal)},{n_split},"
                 f"{med * 1e3:.1f},{avg * 1e3:.1f},{durs[0] * 1e3:.1f},{gbs:.1f},"
                 f"{100 * gbs / PEAK_HBM_GBS:.2f}")
         log(line)
         rows.append(line)
     with open(path, "w") as f:
-        f.write("workload,B,H,Sq,Sk,D,dtype,causal,n_split,us_median,us_avg,us_min,"
+        f.write("workload,B,H,Sq,Sk,D,dtype,kv,causal,n_split,us_median,us_avg,us_min,"
                 "alg_GBps,pct_hbm_peak\n")
         f.write("\n".join(rows) + "\n")
 

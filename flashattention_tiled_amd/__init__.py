@@ -15,8 +15,12 @@ C entry points, re-exported under the same names:
     fa2_rows_per_workgroup(D) -> int
     fa2_fwd_splitkv(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype,
                     n_split, workspace, workspace_bytes, stream) -> int
+    fa2_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale,
+                        k_descale, v_descale, dtype, n_split, workspace,
+                        workspace_bytes, stream) -> int
     fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) -> int
     fa2_splitkv_splits(B, H, Sq, Sk) -> int
+    fa2_splitkv_splits_fp8(B, H, Sq, Sk) -> int
 plus the tensor-level conveniences ``attention(q, k, v, causal, scale)`` (any
 layout whose head dim is contiguous) and
 ``attention_splitkv(q, k, v, causal, scale, n_split)`` (Sq queries against Sk
@@ -50,8 +54,9 @@ FA2_ERR_WORKSPACE = 10
 FA2_ERR_STRIDE = 11
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_supported", "fa2_status_string",
-                    "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
-                    "fa2_splitkv_splits")
+                    "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_fwd_splitkv_fp8",
+                    "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits",
+                    "fa2_splitkv_splits_fp8")
 
 
 class FA2Error(RuntimeError):
@@ -113,10 +118,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa2_fwd_splitkv.restype = i
+    lib.fa2_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, i, i, vp, sz,
+                                        vp]
+    lib.fa2_fwd_splitkv_fp8.restype = i
     lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa2_splitkv_workspace_bytes.restype = sz
     lib.fa2_splitkv_splits.argtypes = [i, i, i, i]
     lib.fa2_splitkv_splits.restype = i
+    lib.fa2_splitkv_splits_fp8.argtypes = [i, i, i, i]
+    lib.fa2_splitkv_splits_fp8.restype = i
     _lib = lib
     return lib
 
@@ -158,8 +168,22 @@ def fa2_fwd_splitkv(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq
                                               workspace, int(workspace_bytes), stream))
 
 
+def fa2_fwd_splitkv_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int,
+                        Sk: int, D: int, causal: int, scale: float, k_descale: float,
+                        v_descale: float, dtype: int, n_split: int, workspace: int,
+                        workspace_bytes: int, stream: int) -> int:
+    """Direct call of the FP8 K/V split-KV entry point; returns the status."""
+    return int(load_library().fa2_fwd_splitkv_fp8(
+        q, k, v, o, lse, B, H, Sq, Sk, D, int(causal), float(scale), float(k_descale),
+        float(v_descale), int(dtype), int(n_split), workspace, int(workspace_bytes), stream))
+
+
 def fa2_splitkv_workspace_bytes(B: int, H: int, Sq: int, Sk: int, D: int, n_split: int) -> int:
     return int(load_library().fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split))
+
+
+def fa2_splitkv_splits_fp8(B: int, H: int, Sq: int, Sk: int) -> int:
+    return int(load_library().fa2_splitkv_splits_fp8(B, H, Sq, Sk))
 
 
 def fa2_splitkv_splits(B: int, H: int, Sq: int, Sk: int) -> int:
@@ -231,12 +255,15 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
 
 
 def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
-                      n_split: int = 0, out=None, lse=None, workspace=None, stream=None):
+                      n_split: int = 0, out=None, lse=None, workspace=None, stream=None,
+                      k_descale: float = 1.0, v_descale: float = 1.0):
     """O, lse for Sq queries against Sk cached keys: q (B, H, Sq, D), k and v
-    (B, H, Sk, D), contiguous CUDA fp16/bf16 tensors. Causal keeps key j for
-    query i iff j <= i + Sk - Sq (the queries are the last Sq positions).
-    n_split = 0 lets the library pick the number of key chunks. `workspace`
-    may be passed preallocated (a CUDA uint8 tensor of at least
+    (B, H, Sk, D), contiguous CUDA tensors. q is fp16 or bf16; k and v have
+    q's dtype, or are both torch.float8_e4m3fn codes whose values are
+    code * k_descale and code * v_descale (fa2_fwd_splitkv_fp8). Causal keeps
+    key j for query i iff j <= i + Sk - Sq (the queries are the last Sq
+    positions). n_split = 0 lets the library pick the number of key chunks.
+    `workspace` may be passed preallocated (a CUDA uint8 tensor of at least
     fa2_splitkv_workspace_bytes bytes); otherwise one is allocated with torch.
     Returns (o like q, lse (B, H, Sq) float32). Raises FA2Error on any
     nonzero status.
@@ -247,8 +274,10 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
             or q.shape[3] != k.shape[3]:
         raise ValueError(f"q must be (B, H, Sq, D) and k, v (B, H, Sk, D), got "
                          f"{tuple(q.shape)}, {tuple(k.shape)}, {tuple(v.shape)}")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k and v must have one dtype")
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    kv8 = fp8 is not None and k.dtype == fp8 and v.dtype == fp8
+    if not (kv8 or q.dtype == k.dtype == v.dtype):
+        raise ValueError("k and v must have q's dtype, or both be float8_e4m3fn")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
@@ -269,15 +298,22 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         stream = torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         if n_split == 0:
-            n_split = fa2_splitkv_splits(B, H, Sq, Sk)
+            n_split = (fa2_splitkv_splits_fp8 if kv8 else fa2_splitkv_splits)(B, H, Sq, Sk)
         need = fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split)
         if workspace is None:
             workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-        status = fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                 lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)),
-                                 float(scale), _dtype_code(q), n_split, workspace.data_ptr(),
-                                 workspace.numel() * workspace.element_size(),
-                                 stream.cuda_stream)
+        ws_bytes = workspace.numel() * workspace.element_size()
+        if kv8:
+            status = fa2_fwd_splitkv_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)),
+                                         float(scale), float(k_descale), float(v_descale),
+                                         _dtype_code(q), n_split, workspace.data_ptr(), ws_bytes,
+                                         stream.cuda_stream)
+        else:
+            status = fa2_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)),
+                                     float(scale), _dtype_code(q), n_split, workspace.data_ptr(),
+                                     ws_bytes, stream.cuda_stream)
     if status != FA2_OK:
         raise FA2Error(status, fa2_status_string(status))
     return out, lse

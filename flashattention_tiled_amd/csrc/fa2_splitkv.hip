@@ -38,11 +38,14 @@ using fa2_host::overlaps;
 
 namespace {
 
-template <int D> struct SplitTile {
+// KV8: K and V hold FP8 e4m3 codes (one byte per element) instead of 16-bit
+// values.
+template <int D, bool KV8 = false> struct SplitTile {
   static constexpr int kBc = 32;
-  static constexpr int kTileBytes = kBc * D * 2;
+  static constexpr int kTileBytes = kBc * D * (KV8 ? 1 : 2);
   static constexpr int kLoadsPerWave = kTileBytes / 1024;  // one wave loads the whole tile
   static constexpr int kLdsBytes = 4 * kTileBytes;         // K and V, two stages each
+  static_assert(kTileBytes % 1024 == 0, "a tile is whole 1 KiB wave loads");
 };
 
 size_t splitkv_part_o_bytes(int B, int H, int Sq, int D, int n_split) {
@@ -51,6 +54,118 @@ size_t splitkv_part_o_bytes(int B, int H, int Sq, int D, int n_split) {
 }
 size_t splitkv_workspace_bytes(int B, int H, int Sq, int D, int n_split) {
   return splitkv_part_o_bytes(B, H, Sq, D, n_split) + (size_t)B * H * n_split * Sq * 3 * sizeof(float);
+}
+
+// ---- FP8 (e4m3) K and V ------------------------------------------------
+// Codes (OCP FP8 e4m3: sign, 4 exponent bits of bias 7, 3 mantissa bits)
+// become matrix-core operands through gfx950's packed conversion, two codes
+// (bytes 0-1, or 2-3, of a word) per instruction, exactly: every e4m3 value
+// is representable in fp16 and in bf16.
+template <int DT>
+__device__ __forceinline__ u32x2 e4m3x4_op(uint32_t x) {
+  if constexpr (DT == FA2_F16) {
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  } else {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  }
+}
+// Eight codes (two words, in byte order) as one operand of element type DT.
+template <int DT>
+__device__ __forceinline__ u32x4 e4m3x8_op(uint32_t x0, uint32_t x1) {
+  const u32x2 a = e4m3x4_op<DT>(x0), b = e4m3x4_op<DT>(x1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// 16-byte chunk swizzles of FP8 tiles (rows of D bytes, D / 16 chunks).
+// K is read 16 bytes per lane, 16 lanes (rows 0-15 or 16-31 of a key block)
+// per cycle: XOR by the row bits above those that already separate rows in
+// the 64 banks. V is read by ds_read_b64_tr_b8, 32 lanes per cycle over 8
+// rows x 2 chunks; an even XOR keeps a chunk pair together and gives each
+// of the 4 rows of one parity (D = 64: of the 2 rows of one residue mod 4;
+// D = 256: each of the 8 rows) its own pair.
+template <int D>
+__device__ __forceinline__ int swz_k8(int row) {
+  return D == 64 ? (row >> 2) & 3 : D == 128 ? (row >> 1) & 7 : row & 15;
+}
+template <int D>
+__device__ __forceinline__ int swz_v8(int row) {
+  return D == 64    ? ((row >> 3) & 1) << 1
+         : D == 128 ? (((row >> 1) & 1) | ((row >> 2) & 2)) << 1
+                    : ((row & 3) | ((row >> 1) & 4)) << 1;
+}
+
+// Per-lane byte offsets of the 16-byte chunks a one-wave FP8 tile load
+// fetches: LDS slot p of the tile receives chunk (p % (D/16)) ^ swz(row) of
+// key row p / (D/16).
+template <int D, int LPW, bool IS_V>
+__device__ __forceinline__ void tile_load_offsets8(int lane, uint32_t (&off)[LPW]) {
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int p = i * 64 + lane;
+    const int r = p / CPR, cp = p % CPR;
+    const int c = cp ^ (IS_V ? swz_v8<D>(r) : swz_k8<D>(r));
+    off[i] = (uint32_t)(r * D + c * 16);
+  }
+}
+
+// S^T = K_t Q^T for an FP8 K tile at byte k_stage: each 16-byte read of row
+// 32 kb + l32 (chunk 2 u + hi) gives the K operands of k-steps 2 u and
+// 2 u + 1, so k-step 2 u + v covers dims 32 u + 16 hi + 8 v .. + 7, the
+// order in which Q^T was loaded.
+template <int D, int DT, int NKB>
+__device__ __forceinline__ void tile_scores_kv8(const unsigned char* smem, uint32_t k_stage,
+                                                int l32, int hi, const u32x4 (&qf)[1][D / 16],
+                                                f32x16 (&acc)[1][NKB]) {
+  using E = Elem<DT>;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) acc[0][kb] = f32x16{};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    const int row = 32 * kb + l32;
+    const unsigned char* rp = smem + k_stage + row * D;
+    const int sw = swz_k8<D>(row);
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const u32x4 raw = *(const u32x4*)(rp + (((2 * u + hi) ^ sw) * 16));
+      acc[0][kb] = E::mfma(e4m3x8_op<DT>(raw[0], raw[1]), qf[0][2 * u], acc[0][kb]);
+      acc[0][kb] = E::mfma(e4m3x8_op<DT>(raw[2], raw[3]), qf[0][2 * u + 1], acc[0][kb]);
+    }
+  }
+}
+
+// O~ += P V for an FP8 V tile at byte v_stage. One ds_read_b64_tr_b8 per
+// (key block, half, head-dim block): in each 16-lane group, output lane i
+// byte e comes from source lane 2 e + i / 8, byte i % 8, so source lane s
+// points at key row R(s / 2) and dims 8 (s % 2) .. + 7 of the group's 16;
+// output lane i then holds dim 16 grp + i for the 8 keys R(0..7). R(e) is
+// the key of P^T element e in this lane half (32 kb + 16 h + 8 (e / 4) +
+// 4 hi + e % 4), so the operands pair up without any exchange.
+template <int D, int DT, int NKB>
+__device__ __forceinline__ void tile_pv_kv8(const unsigned char* smem, uint32_t v_stage,
+                                            uint32_t v8_base, uint32_t v8_x,
+                                            const u32x4 (&pb)[1][NKB][2],
+                                            f32x16 (&acc_o)[1][D / 32]) {
+  using E = Elem<DT>;
+  constexpr int NDB = D / 32;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint32_t a = v_stage + (uint32_t)((32 * kb + 16 * h) * D) + v8_base +
+                           ((uint32_t)(32 * db) ^ v8_x);
+        typedef int i32x2 __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+        const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + a));
+        acc_o[0][db] = E::mfma(e4m3x8_op<DT>((uint32_t)raw[0], (uint32_t)raw[1]), pb[0][kb][h],
+                               acc_o[0][db]);
+      }
 }
 
 // Scale every score of the tile and mask keys at or past `lim` (this lane's
@@ -100,12 +215,15 @@ __device__ __forceinline__ void tile_pv(const unsigned char* smem, uint32_t v_st
   }
 }
 
-template <int D, int DT, bool CAUSAL>
+// c multiplies q . k into base-2 logits; v_mult multiplies O~ before it is
+// stored (1 for 16-bit K and V; for FP8, c carries K's descale and v_mult
+// is V's).
+template <int D, int DT, bool CAUSAL, bool KV8>
 __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int Sq, int Sk, int n_split, int chunk_keys, float c /* scale * log2(e) */) {
-  using ST = SplitTile<D>;
+    const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int Sq, int Sk, int n_split,
+    int chunk_keys, float c, float v_mult) {
+  using ST = SplitTile<D, KV8>;
   constexpr int RB = 1, Bc = ST::kBc, NKB = Bc / 32;
   constexpr int CPR = D / 8, TB = ST::kTileBytes, LPW = ST::kLoadsPerWave;
   constexpr int NDS = D / 16, NDB = D / 32;
@@ -130,24 +248,40 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   // keys this lane's row keeps, within the chunk
   const int row_lim = CAUSAL ? min(k_end, row + off + 1) : k_end;
 
+  // Q^T operands: k-step s covers dims 16 s + 8 hi .. + 7, or, with FP8 K,
+  // dims 32 (s / 2) + 16 hi + 8 (s % 2) .. + 7 (the order its reads give)
   u32x4 qf[RB][NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) {
+    const int d0 = KV8 ? 32 * (s / 2) + 16 * hi + 8 * (s % 2) : 16 * s + 8 * hi;
     qf[0][s] = u32x4{0, 0, 0, 0};
-    if (row < Sq) qf[0][s] = *(const u32x4*)(q + ((size_t)bh * Sq + row) * D + 16 * s + 8 * hi);
+    if (row < Sq) qf[0][s] = *(const u32x4*)(q + ((size_t)bh * Sq + row) * D + d0);
   }
 
-  const uint32_t head_bytes = (uint32_t)Sk * D * 2;
-  const unsigned char* k_head = (const unsigned char*)(k + (size_t)bh * Sk * D);
-  const unsigned char* v_head = (const unsigned char*)(v + (size_t)bh * Sk * D);
+  constexpr int EB = KV8 ? 1 : 2;  // bytes per K or V element
+  const uint32_t head_bytes = (uint32_t)Sk * D * EB;
+  const unsigned char* k_head = (const unsigned char*)k + (size_t)bh * Sk * D * EB;
+  const unsigned char* v_head = (const unsigned char*)v + (size_t)bh * Sk * D * EB;
   uint32_t k_off[LPW], v_off[LPW];
-  tile_load_offsets<D, LPW, false>(0, lane, k_off);
-  tile_load_offsets<D, LPW, true>(0, lane, v_off);
+  if constexpr (KV8) {
+    tile_load_offsets8<D, LPW, false>(lane, k_off);
+    tile_load_offsets8<D, LPW, true>(lane, v_off);
+  } else {
+    tile_load_offsets<D, LPW, false>(0, lane, k_off);
+    tile_load_offsets<D, LPW, true>(0, lane, v_off);
+  }
   const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ swz_k<D>(l32)));
   const int vt_row = 4 * hi + (lane & 15) / 4;
   const int vt_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const uint32_t vt_x = (uint32_t)((vt_row * CPR + vt_chunk) * 16 + 8 * (lane & 1) +
                                    64 * (swz_v<D>(vt_row) >> 2));
+  // FP8 V^T source address of this lane: key row R(e), e = (lane % 16) / 2,
+  // dims 16 grp + 8 (lane % 2) of the 32-dim block, grp = (lane / 16) % 2;
+  // the head-dim block's chunk pair is XORed with the row's swizzle
+  const int e8 = (lane & 15) >> 1, grp8 = (lane >> 4) & 1;
+  const int r8 = 8 * (e8 >> 2) + 4 * hi + (e8 & 3);
+  const uint32_t v8_base = (uint32_t)(r8 * D + 16 * grp8 + 8 * (lane & 1));
+  const uint32_t v8_x = (uint32_t)(16 * swz_v8<D>(r8));
 
   f32x16 acc_o[RB][NDB];
 #pragma unroll
@@ -171,7 +305,10 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
       load_tile<LPW, TB>(v_head, head_bytes, t_first + t + 1, smem + (vs ^ TB), 0, v_off);
     }
     f32x16 sc[RB][NKB];
-    tile_scores<D, DT, RB, NKB>(smem, ks, k_lane, qf, sc);
+    if constexpr (KV8)
+      tile_scores_kv8<D, DT, NKB>(smem, ks, l32, hi, qf, sc);
+    else
+      tile_scores<D, DT, RB, NKB>(smem, ks, k_lane, qf, sc);
     tile_mask_lim<NKB>(sc, (t_first + t) * Bc, row_lim, c, hi);
     float tm[RB];
     tile_max<RB, NKB>(sc, one, tm);
@@ -190,7 +327,14 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
     tile_probs<DT, RB, NKB>(sc, one, m_ref, tsum, trnd, pb);
     l_run[0] += tsum[0];
     l_rnd[0] += trnd[0];
-    tile_pv<D, DT, RB, NKB>(smem, vs, vt_x, pb, acc_o);
+    if constexpr (KV8)
+      tile_pv_kv8<D, DT, NKB>(smem, vs, v8_base, v8_x, pb, acc_o);
+    else
+      tile_pv<D, DT, RB, NKB>(smem, vs, vt_x, pb, acc_o);
+  }
+  if constexpr (KV8) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc_o[0][db] *= v_mult;
   }
 
   // partial state of rows < Sq
@@ -261,13 +405,14 @@ __global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
 }
 
 // Key chunks per (b, h) for a launch: enough workgroups for about two on
-// every compute unit (decoding is bandwidth bound; each one-wave workgroup
-// keeps a K and a V tile in flight), each chunk at least 4 tiles long.
-int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu) {
+// every compute unit with 16-bit K and V, four with FP8 (a chunk then holds
+// half the bytes, and the code conversions want more waves beside the
+// loads), each chunk at least 4 tiles long. Measured on decode shapes: more,
+// shorter chunks lose bandwidth.
+int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu, bool kv8) {
   const long long n_qblk = (Sq + 31) / 32;
   const long long n_tiles = (Sk + SplitTile<64>::kBc - 1) / SplitTile<64>::kBc;
-  // measured on decode shapes: more, shorter chunks lose bandwidth
-  const long long target = 2LL * n_cu;
+  const long long target = (kv8 ? 4LL : 2LL) * n_cu;
   long long want = (target + (long long)B * H * n_qblk - 1) / ((long long)B * H * n_qblk);
   const long long cap = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
   if (want > cap) want = cap;
@@ -276,11 +421,13 @@ int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu) {
   return (int)want;
 }
 
-template <int D, int DT, bool CAUSAL>
+// Launch the partial and combine kernels. kv8: K and V are FP8 codes with
+// these descales (k_mult, v_mult), else 16-bit values (both 1).
+template <int D, int DT, bool CAUSAL, bool KV8>
 hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                          int H, int Sq, int Sk, float scale, int n_split, void* ws,
-                          hipStream_t stream) {
-  using ST = SplitTile<D>;
+                          int H, int Sq, int Sk, float scale, float k_mult, float v_mult,
+                          int n_split, void* ws, hipStream_t stream) {
+  using ST = SplitTile<D, KV8>;
   // chunks of whole tiles; trailing splits that would be empty are dropped
   const int n_tiles = (Sk + ST::kBc - 1) / ST::kBc;
   const int chunk_tiles = (n_tiles + n_split - 1) / n_split;
@@ -289,9 +436,9 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, 
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + splitkv_part_o_bytes(B, H, Sq, D, n_eff));
   const dim3 grid((unsigned)(n_eff * n_qblk), (unsigned)H, (unsigned)B);
-  fa2_splitkv_partial_kernel<D, DT, CAUSAL><<<grid, dim3(64), 0, stream>>>(
-      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, part_o, part_ml, Sq, Sk, n_eff,
-      chunk_tiles * ST::kBc, scale * kLog2e);
+  fa2_splitkv_partial_kernel<D, DT, CAUSAL, KV8><<<grid, dim3(64), 0, stream>>>(
+      (const uint16_t*)q, k, v, part_o, part_ml, Sq, Sk, n_eff, chunk_tiles * ST::kBc,
+      scale * kLog2e * k_mult, v_mult);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_rows = B * H * Sq;
@@ -300,44 +447,53 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, 
   return hipGetLastError();
 }
 
-template <int D, int DT>
+template <int D, int DT, bool KV8>
 hipError_t launch_splitkv_causal(int causal, const void* q, const void* k, const void* v, void* o,
                                  float* lse, int B, int H, int Sq, int Sk, float scale,
-                                 int n_split, void* ws, hipStream_t stream) {
-  return causal ? launch_splitkv<D, DT, true>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_split, ws, stream)
-                : launch_splitkv<D, DT, false>(q, k, v, o, lse, B, H, Sq, Sk, scale, n_split, ws, stream);
+                                 float k_mult, float v_mult, int n_split, void* ws,
+                                 hipStream_t stream) {
+  return causal ? launch_splitkv<D, DT, true, KV8>(q, k, v, o, lse, B, H, Sq, Sk, scale, k_mult,
+                                                   v_mult, n_split, ws, stream)
+                : launch_splitkv<D, DT, false, KV8>(q, k, v, o, lse, B, H, Sq, Sk, scale, k_mult,
+                                                    v_mult, n_split, ws, stream);
 }
 
-template <int D>
+template <int D, bool KV8>
 hipError_t launch_splitkv_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                                 void* o, float* lse, int B, int H, int Sq, int Sk, float scale,
-                                int n_split, void* ws, hipStream_t stream) {
-  return dtype == FA2_F16 ? launch_splitkv_causal<D, FA2_F16>(causal, q, k, v, o, lse, B, H, Sq, Sk,
-                                                               scale, n_split, ws, stream)
-                          : launch_splitkv_causal<D, FA2_BF16>(causal, q, k, v, o, lse, B, H, Sq,
-                                                                Sk, scale, n_split, ws, stream);
+                                float k_mult, float v_mult, int n_split, void* ws,
+                                hipStream_t stream) {
+  return dtype == FA2_F16
+             ? launch_splitkv_causal<D, FA2_F16, KV8>(causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
+                                                      k_mult, v_mult, n_split, ws, stream)
+             : launch_splitkv_causal<D, FA2_BF16, KV8>(causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
+                                                       k_mult, v_mult, n_split, ws, stream);
 }
 
-}  // namespace
-
-extern "C" int fa2_splitkv_splits(int B, int H, int Sq, int Sk) {
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return 1;
-  int n_cu = 0;
-  if (check_device(&n_cu) != FA2_OK) n_cu = 256;
-  return splitkv_default_splits(B, H, Sq, Sk, n_cu);
+template <bool KV8>
+hipError_t launch_splitkv_any(int D, int dtype, int causal, const void* q, const void* k,
+                              const void* v, void* o, float* lse, int B, int H, int Sq, int Sk,
+                              float scale, float k_mult, float v_mult, int n_split, void* ws,
+                              hipStream_t stream) {
+  switch (D) {
+    case 64:
+      return launch_splitkv_dtype<64, KV8>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
+                                           k_mult, v_mult, n_split, ws, stream);
+    case 128:
+      return launch_splitkv_dtype<128, KV8>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
+                                            k_mult, v_mult, n_split, ws, stream);
+    default:
+      return launch_splitkv_dtype<256, KV8>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
+                                            k_mult, v_mult, n_split, ws, stream);
+  }
 }
 
-extern "C" size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int n_split) {
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || n_split < 0) return 0;
-  if (!(D == 64 || D == 128 || D == 256)) return 0;
-  if (n_split == 0) n_split = fa2_splitkv_splits(B, H, Sq, Sk);
-  return splitkv_workspace_bytes(B, H, Sq, D, n_split);
-}
-
-extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int Sq, int Sk, int D, int causal, float scale,
-                               int dtype, int n_split, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+// Checks shared by the two split-KV entry points, in the documented order,
+// and the launch. kv_elem_bytes: 2 for 16-bit K and V, 1 for FP8.
+int splitkv_call(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Sq, int Sk, int D, int causal, float scale, int dtype, float k_descale,
+                 float v_descale, int kv_elem_bytes, int n_split, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || B > 65535 || H > 65535 || n_split < 0)
     return FA2_ERR_SHAPE;
@@ -346,11 +502,14 @@ extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void
   if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
   // one head of K or V, plus a tile past its end, within 32-bit byte offsets;
   // query rows of the whole call indexed in 32 bits
-  if (((long long)Sk + 256) * D * 2 > (long long)INT32_MAX) return FA2_ERR_SHAPE;
+  if (((long long)Sk + 256) * D * kv_elem_bytes > (long long)INT32_MAX) return FA2_ERR_SHAPE;
   if ((long long)B * H * Sq > (long long)INT32_MAX / 4) return FA2_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
   if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
+  if (!std::isfinite(k_descale) || !(k_descale > 0.f) || !std::isfinite(v_descale) ||
+      !(v_descale > 0.f))
+    return FA2_ERR_SCALE;
   // the default split count needs the device's size; an explicit one lets
   // every argument be checked before the device is looked up
   int n_cu = 0;
@@ -359,12 +518,13 @@ extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void
     const int dev = check_device(&n_cu);
     if (dev != FA2_OK) return dev;
     device_checked = true;
-    n_split = splitkv_default_splits(B, H, Sq, Sk, n_cu);
+    n_split = splitkv_default_splits(B, H, Sq, Sk, n_cu, kv_elem_bytes == 1);
   }
   if (n_split > 65536) return FA2_ERR_SHAPE;
   const size_t need = splitkv_workspace_bytes(B, H, Sq, D, n_split);
   if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return FA2_ERR_WORKSPACE;
-  const size_t q_bytes = (size_t)B * H * Sq * D * 2, kv_bytes = (size_t)B * H * Sk * D * 2;
+  const size_t q_bytes = (size_t)B * H * Sq * D * 2;
+  const size_t kv_bytes = (size_t)B * H * Sk * D * kv_elem_bytes;
   const size_t lse_bytes = (size_t)B * H * Sq * sizeof(float);
   if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
       overlaps(o, q_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, q_bytes) ||
@@ -379,21 +539,57 @@ extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void
   }
 
   (void)hipGetLastError();
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t err;
-  switch (D) {
-    case 64:
-      err = launch_splitkv_dtype<64>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, n_split,
-                                     workspace, st);
-      break;
-    case 128:
-      err = launch_splitkv_dtype<128>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, n_split,
-                                      workspace, st);
-      break;
-    default:
-      err = launch_splitkv_dtype<256>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, n_split,
-                                      workspace, st);
-      break;
-  }
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t err =
+      kv_elem_bytes == 1
+          ? launch_splitkv_any<true>(D, dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
+                                     k_descale, v_descale, n_split, workspace, st)
+          : launch_splitkv_any<false>(D, dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, 1.f,
+                                      1.f, n_split, workspace, st);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+namespace {
+int default_splits_here(int B, int H, int Sq, int Sk, bool kv8) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return 1;
+  int n_cu = 0;
+  if (check_device(&n_cu) != FA2_OK) n_cu = 256;
+  return splitkv_default_splits(B, H, Sq, Sk, n_cu, kv8);
+}
+}  // namespace
+
+extern "C" int fa2_splitkv_splits(int B, int H, int Sq, int Sk) {
+  return default_splits_here(B, H, Sq, Sk, false);
+}
+
+extern "C" int fa2_splitkv_splits_fp8(int B, int H, int Sq, int Sk) {
+  return default_splits_here(B, H, Sq, Sk, true);
+}
+
+extern "C" size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int n_split) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || n_split < 0) return 0;
+  if (!(D == 64 || D == 128 || D == 256)) return 0;
+  // n_split = 0: enough for the default of either entry point (the FP8
+  // default is never below the 16-bit one)
+  if (n_split == 0) n_split = default_splits_here(B, H, Sq, Sk, true);
+  return splitkv_workspace_bytes(B, H, Sq, D, n_split);
+}
+
+extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                               int dtype, int n_split, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype, 1.f, 1.f, 2, n_split,
+                      workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa2_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, int B, int H, int Sq, int Sk, int D, int causal,
+                                   float scale, float k_descale, float v_descale, int dtype,
+                                   int n_split, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype, k_descale, v_descale,
+                      1, n_split, workspace, workspace_bytes, stream);
 }

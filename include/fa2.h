@@ -170,14 +170,43 @@ int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float 
                     int dtype, int n_split, void *workspace,
                     size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace fa2_fwd_splitkv needs for these sizes and n_split
- * (0 = the default split count); 0 for invalid sizes or head dims. */
+/*
+ * fa2_fwd_splitkv_fp8 -- fa2_fwd_splitkv with K and V in FP8: a KV cache of
+ * OCP e4m3 codes (1 sign, 4 exponent bits of bias 7, 3 mantissa bits; one
+ * byte per element) with one descale per tensor, the element values being
+ * code * k_descale and code * v_descale. This is the FP8 direction the
+ * infra.bea.ai guide names for FlashAttention-3 ("FlashAttention-3 and
+ * Beyond"), taken where MI355X gains from it without rounding anything
+ * more: decoding is bound by the bytes of K and V it reads, and FP8 halves
+ * them. The codes convert exactly to fp16 or bf16 (q's dtype) on the GPU,
+ * so the arithmetic and the result are those of fa2_fwd_splitkv on the
+ * dequantized K and V (up to the order of the fp32 sums in q . k).
+ *
+ * k, v      (B, H, Sk, D) contiguous e4m3 codes, 16-byte aligned. The NaN
+ *           codes 0x7f and 0xff make the rows that see them NaN.
+ * k_descale, v_descale  finite and > 0 (FA2_ERR_SCALE otherwise).
+ * q, o, lse, the other arguments, the workspace (its size does not depend
+ * on the element type of K and V) and the return codes are those of
+ * fa2_fwd_splitkv; dtype is that of q and o.
+ */
+int fa2_fwd_splitkv_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                        float k_descale, float v_descale, int dtype, int n_split,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fa2_fwd_splitkv and fa2_fwd_splitkv_fp8 need for these
+ * sizes and n_split; n_split = 0 gives enough for the default split count
+ * of either. 0 for invalid sizes or head dims. */
 size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int D, int n_split);
 
-/* The default number of key chunks per (b, h): enough workgroups for about
- * two on every compute unit of the current device, each chunk at least four
- * 32-key tiles; 1 for invalid sizes. */
+/* The default number of key chunks per (b, h) of fa2_fwd_splitkv: enough
+ * workgroups for about two on every compute unit of the current device,
+ * each chunk at least four 32-key tiles; 1 for invalid sizes. */
 int fa2_splitkv_splits(int B, int H, int Sq, int Sk);
+
+/* The same for fa2_fwd_splitkv_fp8: about four workgroups per compute unit
+ * (a chunk of FP8 K and V holds half the bytes). */
+int fa2_splitkv_splits_fp8(int B, int H, int Sq, int Sk);
 
 #ifdef __cplusplus
 }

@@ -309,6 +309,42 @@ def test_splitkv_validation_status(lib, kw, status):
     assert _call_splitkv(**kw) == status
 
 
+def _call_splitkv_fp8(**kw):
+    args = dict(q=QS, k=KS, v=VS, o=OS, lse=LS, B=1, H=1, Sq=_SQ, Sk=_SK, D=_D, causal=0,
+                scale=0.125, k_descale=0.01, v_descale=0.02, dtype=fa.FA2_F16, n_split=4,
+                workspace=WS, workspace_bytes=_ws_bytes(4), stream=None)
+    args.update(kw)
+    return fa.fa2_fwd_splitkv_fp8(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), fa.FA2_ERR_NULL),
+    (dict(Sk=0), fa.FA2_ERR_SHAPE),
+    (dict(causal=1, Sq=_SK + 1), fa.FA2_ERR_SHAPE),
+    (dict(dtype=5), fa.FA2_ERR_DTYPE),
+    (dict(D=32), fa.FA2_ERR_HEADDIM),
+    (dict(v=VS + 4), fa.FA2_ERR_ALIGN),
+    (dict(k_descale=0.0), fa.FA2_ERR_SCALE),
+    (dict(v_descale=-1.0), fa.FA2_ERR_SCALE),
+    (dict(k_descale=float("nan")), fa.FA2_ERR_SCALE),
+    (dict(v_descale=float("inf")), fa.FA2_ERR_SCALE),
+    (dict(workspace_bytes=_ws_bytes(4) - 1), fa.FA2_ERR_WORKSPACE),
+    (dict(o=KS + 8 * _D), fa.FA2_ERR_ALIAS),
+])
+def test_splitkv_fp8_validation_status(lib, kw, status):
+    assert _call_splitkv_fp8(**kw) == status
+
+
+def test_splitkv_fp8_kv_extent_is_one_byte_per_element(lib):
+    # o just past the FP8 K (Sk * D bytes) does not overlap it; one element
+    # earlier does
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call_splitkv_fp8(o=KS + _SK * _D) == fa.FA2_ERR_NO_DEVICE
+    assert _call_splitkv_fp8(o=KS + _SK * _D - 16) == fa.FA2_ERR_ALIAS
+
+
 def test_splitkv_no_device_status_without_gpu(lib):
     import torch
     if torch.cuda.device_count() > 0:

@@ -87,6 +87,10 @@ class DecodeWorkload:
     dtype: str
     causal: bool
     qk_mult: float = 1.0
+    # "e4m3": K and V are FP8 codes with per-tensor descales (else q's dtype)
+    kv: str = ""
+    k_descale: float = 1.0
+    v_descale: float = 1.0
 
     @property
     def scale(self) -> float:
@@ -104,8 +108,9 @@ class DecodeWorkload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """K and V read once, Q read once, O written once, lse written once."""
-        kv = 2 * self.B * self.H * self.Sk * self.D * 2
+        """K and V read once (1 byte per element for FP8), Q read once, O
+        written once, lse written once."""
+        kv = 2 * self.B * self.H * self.Sk * self.D * (1 if self.kv == "e4m3" else 2)
         qo = 2 * self.B * self.H * self.Sq * self.D * 2
         return kv + qo + self.B * self.H * self.Sq * 4
 
@@ -126,12 +131,44 @@ def make_qkv_decode(w: DecodeWorkload, seed: int = 0):
     return q.to(dt), k.to(dt), v.to(dt)
 
 
+def make_qkv_decode_fp8(w: DecodeWorkload, seed: int = 0):
+    """q as make_qkv_decode draws it, and k and v as FP8 e4m3 codes: the same
+    fp32 draws divided by the workload's descales and cast once to
+    torch.float8_e4m3fn (round to nearest, saturating at 448). Returns
+    (q, k_codes, v_codes); the values they stand for are codes * descale."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((w.B, w.H, w.Sq, w.D), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.H, w.Sk, w.D), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.H, w.Sk, w.D), generator=g, dtype=torch.float32)
+    if w.qk_mult != 1.0:
+        q = q * w.qk_mult
+        k = k * w.qk_mult
+    f8 = torch.float8_e4m3fn
+    k8 = (k / w.k_descale).clamp(-448.0, 448.0).to(f8)
+    v8 = (v / w.v_descale).clamp(-448.0, 448.0).to(f8)
+    return q.to(w.torch_dtype), k8, v8
+
+
+def dequantize_fp8(codes, descale: float):
+    """The values FP8 codes stand for, in fp64 (exact)."""
+    return codes.to(torch.float64) * float(descale)
+
+
 # Decoding against a long KV cache (split-KV path): one new token per
 # sequence, and a speculative/chunked step of 16 new tokens, bf16 and fp16.
 DECODE = [
     DecodeWorkload("decode_b8_h32_sk32768_d128", 8, 32, 1, 32768, 128, "bf16", True),
     DecodeWorkload("decode_b1_h32_sk131072_d128", 1, 32, 1, 131072, 128, "f16", True),
     DecodeWorkload("decode_b4_h32_sq16_sk16384_d128", 4, 32, 16, 16384, 128, "bf16", True),
+]
+
+# The same shapes against an FP8 KV cache (descale 1/64: N(0, 1) values map
+# to codes up to about 320 of e4m3's 448).
+DECODE_FP8 = [
+    DecodeWorkload(w.name + "_kv8", w.B, w.H, w.Sq, w.Sk, w.D, w.dtype, w.causal, kv="e4m3",
+                   k_descale=1 / 64, v_descale=1 / 64)
+    for w in DECODE
 ]
 
 
