@@ -60,7 +60,8 @@ def read_traffic(workload_name: str):
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     text = open(TRAFFIC_SUMMARY).read()
-    fields = dict(re.findall(r"^- (\w+): `?([^`\n]+)`?$", text, flags=re.M))
+    # "- key: `value`" lines, possibly followed by a note
+    fields = dict(re.findall(r"^- (\w+): `([^`\n]+)`", text, flags=re.M))
     same_source = fields.get("kernel_sources_sha256") == kernel_source_sha()
     same_library = fields.get("library_sha256", "-") == library_sha()
     if not (same_source or same_library):

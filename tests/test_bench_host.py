@@ -1,0 +1,27 @@
+"""Host-side pieces of bench.py (no GPU): reading the HBM traffic figure
+from a rocprofv3 counter summary, keyed to the kernel sources it measured."""
+import bench
+
+
+def _summary(tmp_path, sha, workload="sweep_s8192_d128", traffic="715306817"):
+    p = tmp_path / "counters.md"
+    p.write_text(
+        "# rocprofv3 HBM byte counters\n\n"
+        f"- traffic_bytes_per_launch: `{traffic}`\n"
+        f"- kernel_sources_sha256: `{sha}` (fa2_tile.h, fa2_fwd.hip)\n"
+        "- library_sha256: `0000`\n"
+        f"- workload: `{workload}`\n")
+    return str(p)
+
+
+def test_traffic_read_when_the_sources_match(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", _summary(tmp_path, bench.kernel_source_sha()))
+    assert bench.read_traffic("sweep_s8192_d128") == 715306817.0
+
+
+def test_traffic_null_for_other_sources_or_workload(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", _summary(tmp_path, "f" * 64))
+    assert bench.read_traffic("sweep_s8192_d128") is None
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY",
+                        _summary(tmp_path, bench.kernel_source_sha(), workload="other"))
+    assert bench.read_traffic("sweep_s8192_d128") is None
