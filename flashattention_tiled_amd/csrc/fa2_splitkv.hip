@@ -359,7 +359,9 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
 }
 
 // Merge the chunks of each query row: one wave per row, D / 64 columns per
-// lane.
+// lane. The chunks' (m, l, l') are read 64 at a time, one chunk per lane,
+// and reduced across the wave; the weighted O~ rows are then summed four
+// chunks at a time, so that their loads overlap.
 template <int D, int DT>
 __global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ o,
@@ -371,24 +373,56 @@ __global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
   if (r >= n_rows) return;  // whole waves leave together
   const int bh = r / Sq, i = r % Sq;
   const size_t first = (size_t)bh * n_split * Sq + i;  // partial row of chunk 0
+  // M = max of m over the chunks that saw a key
   float mx = -INFINITY;
-  for (int g = 0; g < n_split; ++g) {
+  for (int g = lane; g < n_split; g += 64) {
     const float* ml = part_ml + (first + (size_t)g * Sq) * 3;
     if (ml[2] > 0.f) mx = fmaxf(mx, ml[0]);
   }
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
   float num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
   float den = 0.f, lsum = 0.f;
-  for (int g = 0; g < n_split; ++g) {
-    const size_t prow = first + (size_t)g * Sq;
-    const float* ml = part_ml + prow * 3;
-    const float w = ml[2] > 0.f ? __builtin_amdgcn_exp2f(ml[0] - mx) : 0.f;
-    lsum += w * ml[1];
-    den += w * ml[2];
-    const float* po = part_o + prow * D;
+  for (int g0 = 0; g0 < n_split; g0 += 64) {
+    // this lane's chunk of the block: w = 2^(m - M), and its share of the sums
+    float w = 0.f;
+    if (g0 + lane < n_split) {
+      const float* ml = part_ml + (first + (size_t)(g0 + lane) * Sq) * 3;
+      if (ml[2] > 0.f) {
+        w = __builtin_amdgcn_exp2f(ml[0] - mx);
+        lsum += w * ml[1];
+        den += w * ml[2];
+      }
+    }
+    const int nb = min(64, n_split - g0);
+    int j = 0;
+    for (; j + 4 <= nb; j += 4) {
+      float wj[4], val[4][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += w * po[lane * PER + e];
+      for (int u = 0; u < 4; ++u) {
+        wj[u] = __shfl(w, j + u);
+        const float* po = part_o + (first + (size_t)(g0 + j + u) * Sq) * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) val[u][e] = po[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) num[e] += wj[u] * val[u][e];
+    }
+    for (; j < nb; ++j) {
+      const float wj = __shfl(w, j);
+      const float* po = part_o + (first + (size_t)(g0 + j) * Sq) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += wj * po[e];
+    }
+  }
+#pragma unroll
+  for (int s = 32; s > 0; s >>= 1) {
+    lsum += __shfl_xor(lsum, s);
+    den += __shfl_xor(den, s);
   }
   const float inv = 1.0f / den;
   uint16_t* orow = o + (size_t)r * D;
