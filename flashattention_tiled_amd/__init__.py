@@ -18,6 +18,9 @@ C entry points, re-exported under the same names:
     fa2_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale,
                         k_descale, v_descale, dtype, n_split, workspace,
                         workspace_bytes, stream) -> int
+    fa2_fwd_splitkv_strided(q, k, v, o, lse, B, H, Sq, Sk, D, strides, causal,
+                            scale, dtype, kv_fp8, k_descale, v_descale, n_split,
+                            workspace, workspace_bytes, stream) -> int
     fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) -> int
     fa2_splitkv_splits(B, H, Sq, Sk) -> int
     fa2_splitkv_splits_fp8(B, H, Sq, Sk) -> int
@@ -55,6 +58,7 @@ FA2_ERR_STRIDE = 11
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_supported", "fa2_status_string",
                     "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_fwd_splitkv_fp8",
+                    "fa2_fwd_splitkv_strided",
                     "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits",
                     "fa2_splitkv_splits_fp8")
 
@@ -121,6 +125,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, i, i, vp, sz,
                                         vp]
     lib.fa2_fwd_splitkv_fp8.restype = i
+    lib.fa2_fwd_splitkv_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i,
+                                            ctypes.POINTER(ctypes.c_longlong), i, f, i, i, f, f,
+                                            i, vp, sz, vp]
+    lib.fa2_fwd_splitkv_strided.restype = i
     lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa2_splitkv_workspace_bytes.restype = sz
     lib.fa2_splitkv_splits.argtypes = [i, i, i, i]
@@ -176,6 +184,19 @@ def fa2_fwd_splitkv_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int
     return int(load_library().fa2_fwd_splitkv_fp8(
         q, k, v, o, lse, B, H, Sq, Sk, D, int(causal), float(scale), float(k_descale),
         float(v_descale), int(dtype), int(n_split), workspace, int(workspace_bytes), stream))
+
+
+def fa2_fwd_splitkv_strided(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int,
+                            Sk: int, D: int, strides, causal: int, scale: float, dtype: int,
+                            kv_fp8: int, k_descale: float, v_descale: float, n_split: int,
+                            workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Direct call of the strided split-KV entry point; `strides` is a
+    sequence of 12 element strides (batch, head, seq of q, k, v, o)."""
+    st = None if strides is None else (ctypes.c_longlong * 12)(*[int(x) for x in strides])
+    return int(load_library().fa2_fwd_splitkv_strided(
+        q, k, v, o, lse, B, H, Sq, Sk, D, st, int(causal), float(scale), int(dtype), int(kv_fp8),
+        float(k_descale), float(v_descale), int(n_split), workspace, int(workspace_bytes),
+        stream))
 
 
 def fa2_splitkv_workspace_bytes(B: int, H: int, Sq: int, Sk: int, D: int, n_split: int) -> int:
@@ -258,7 +279,8 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
                       n_split: int = 0, out=None, lse=None, workspace=None, stream=None,
                       k_descale: float = 1.0, v_descale: float = 1.0):
     """O, lse for Sq queries against Sk cached keys: q (B, H, Sq, D), k and v
-    (B, H, Sk, D), contiguous CUDA tensors. q is fp16 or bf16; k and v have
+    (B, H, Sk, D), CUDA tensors with a contiguous last dim (other strides
+    free: fa2_fwd_splitkv_strided). q is fp16 or bf16; k and v have
     q's dtype, or are both torch.float8_e4m3fn codes whose values are
     code * k_descale and code * v_descale (fa2_fwd_splitkv_fp8). Causal keeps
     key j for query i iff j <= i + Sk - Sq (the queries are the last Sq
@@ -280,22 +302,23 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         raise ValueError("k and v must have q's dtype, or both be float8_e4m3fn")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k and v must be contiguous")
+    if not (q.stride(3) == 1 and k.stride(3) == 1 and v.stride(3) == 1):
+        raise ValueError("q, k and v must have a contiguous last (head) dim")
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
+    if out.shape != q.shape or out.dtype != q.dtype or out.stride(3) != 1:
+        raise ValueError("out must be a tensor like q with a contiguous last dim")
     if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, H, Sq) tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
+    contiguous = all(t.is_contiguous() for t in (q, k, v, out))
     with torch.cuda.device(q.device):
         if n_split == 0:
             n_split = (fa2_splitkv_splits_fp8 if kv8 else fa2_splitkv_splits)(B, H, Sq, Sk)
@@ -303,7 +326,14 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         if workspace is None:
             workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
         ws_bytes = workspace.numel() * workspace.element_size()
-        if kv8:
+        if not contiguous:
+            strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]
+            status = fa2_fwd_splitkv_strided(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                Sq, Sk, D, strides, int(bool(causal)), float(scale), _dtype_code(q), int(kv8),
+                float(k_descale), float(v_descale), n_split, workspace.data_ptr(), ws_bytes,
+                stream.cuda_stream)
+        elif kv8:
             status = fa2_fwd_splitkv_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          lse.data_ptr(), B, H, Sq, Sk, D, int(bool(causal)),
                                          float(scale), float(k_descale), float(v_descale),

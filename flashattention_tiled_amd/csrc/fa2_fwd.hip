@@ -42,7 +42,9 @@
 #include "fa2_host.h"
 
 using fa2_host::check_device;
+using fa2_host::extent_bytes;
 using fa2_host::overlaps;
+using fa2_host::rows_disjoint;
 
 namespace {
 
@@ -605,35 +607,6 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
   }
 }
 
-// Whether the rows (b, h, s) of a (B, H, S, D) tensor with these element
-// strides (head dim contiguous) are pairwise disjoint: taking the dims of
-// size > 1 in ascending stride order, each stride must reach past the span
-// of the dims before it.
-bool rows_disjoint(int B, int H, int S, int D, long long sb, long long sh, long long ss) {
-  long long n[3] = {B, H, S}, st[3] = {sb, sh, ss};
-  for (int i = 1; i < 3; ++i)
-    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
-      const long long tn = n[j], ts = st[j];
-      n[j] = n[j - 1];
-      st[j] = st[j - 1];
-      n[j - 1] = tn;
-      st[j - 1] = ts;
-    }
-  long long span = D;
-  for (int i = 0; i < 3; ++i) {
-    if (n[i] < 2) continue;
-    if (st[i] < span) return false;
-    span += st[i] * (n[i] - 1);
-  }
-  return true;
-}
-
-// Bytes from a tensor's base pointer to the end of its last element.
-size_t extent_bytes(int B, int H, int S, int D, long long sb, long long sh, long long ss) {
-  return (size_t)(((long long)(B - 1) * sb + (long long)(H - 1) * sh + (long long)(S - 1) * ss +
-                   D) * 2);
-}
-
 }  // namespace
 
 static_assert(Shape<64, true>::kBr == Shape<64>::kBr,
@@ -715,10 +688,10 @@ extern "C" int fa2_fwd_strided(const void* q, const void* k, const void* v, void
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
   if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
   // overlap of the outputs with anything, by the byte ranges the tensors span
-  const size_t qe = extent_bytes(B, H, S, D, st.qb, st.qh, st.qs);
-  const size_t ke = extent_bytes(B, H, S, D, st.kb, st.kh, st.ks);
-  const size_t ve = extent_bytes(B, H, S, D, st.vb, st.vh, st.vs);
-  const size_t oe = extent_bytes(B, H, S, D, st.ob, st.oh, st.os);
+  const size_t qe = extent_bytes(B, H, S, D, st.qb, st.qh, st.qs, 2);
+  const size_t ke = extent_bytes(B, H, S, D, st.kb, st.kh, st.ks, 2);
+  const size_t ve = extent_bytes(B, H, S, D, st.vb, st.vh, st.vs, 2);
+  const size_t oe = extent_bytes(B, H, S, D, st.ob, st.oh, st.os, 2);
   const size_t lse_bytes = (size_t)B * H * S * sizeof(float);
   if (overlaps(o, oe, q, qe) || overlaps(o, oe, k, ke) || overlaps(o, oe, v, ve) ||
       overlaps(lse, lse_bytes, q, qe) || overlaps(lse, lse_bytes, k, ke) ||

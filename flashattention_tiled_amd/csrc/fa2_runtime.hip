@@ -48,6 +48,33 @@ int check_device(int* n_cu) {
   return verdict == 1 ? FA2_OK : FA2_ERR_NO_DEVICE;
 }
 
+// Taking the dims of size > 1 in ascending stride order, each stride must
+// reach past the span of the dims before it.
+bool rows_disjoint(int B, int H, int S, int D, long long sb, long long sh, long long ss) {
+  long long n[3] = {B, H, S}, st[3] = {sb, sh, ss};
+  for (int i = 1; i < 3; ++i)
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      const long long tn = n[j], ts = st[j];
+      n[j] = n[j - 1];
+      st[j] = st[j - 1];
+      n[j - 1] = tn;
+      st[j - 1] = ts;
+    }
+  long long span = D;
+  for (int i = 0; i < 3; ++i) {
+    if (n[i] < 2) continue;
+    if (st[i] < span) return false;
+    span += st[i] * (n[i] - 1);
+  }
+  return true;
+}
+
+size_t extent_bytes(int B, int H, int S, int D, long long sb, long long sh, long long ss,
+                    int elem_bytes) {
+  return (size_t)(((long long)(B - 1) * sb + (long long)(H - 1) * sh + (long long)(S - 1) * ss +
+                   D) * elem_bytes);
+}
+
 }  // namespace fa2_host
 
 extern "C" int fa2_supported(int D, int dtype) {

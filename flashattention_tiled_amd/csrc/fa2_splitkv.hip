@@ -34,7 +34,9 @@
 #include "fa2_host.h"
 
 using fa2_host::check_device;
+using fa2_host::extent_bytes;
 using fa2_host::overlaps;
+using fa2_host::rows_disjoint;
 
 namespace {
 
@@ -99,17 +101,18 @@ __device__ __forceinline__ int swz_v8(int row) {
 }
 
 // Per-lane byte offsets of the 16-byte chunks a one-wave FP8 tile load
-// fetches: LDS slot p of the tile receives chunk (p % (D/16)) ^ swz(row) of
-// key row p / (D/16).
+// fetches from key rows `row_bytes` apart: LDS slot p of the tile receives
+// chunk (p % (D/16)) ^ swz(row) of key row p / (D/16).
 template <int D, int LPW, bool IS_V>
-__device__ __forceinline__ void tile_load_offsets8(int lane, uint32_t (&off)[LPW]) {
+__device__ __forceinline__ void tile_load_offsets8(int lane, uint32_t row_bytes,
+                                                   uint32_t (&off)[LPW]) {
   constexpr int CPR = D / 16;
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int p = i * 64 + lane;
     const int r = p / CPR, cp = p % CPR;
     const int c = cp ^ (IS_V ? swz_v8<D>(r) : swz_k8<D>(r));
-    off[i] = (uint32_t)(r * D + c * 16);
+    off[i] = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
   }
 }
 
@@ -215,6 +218,17 @@ __device__ __forceinline__ void tile_pv(const unsigned char* smem, uint32_t v_st
   }
 }
 
+// Element strides of the batch, head and sequence dims of Q, K, V and O
+// (the head dim is contiguous; FP8 K and V count bytes).
+struct SkvStrides {
+  long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
+};
+
+SkvStrides contiguous_strides(int H, int Sq, int Sk, int D) {
+  const long long q_h = (long long)Sq * D, k_h = (long long)Sk * D;
+  return SkvStrides{H * q_h, q_h, D, H * k_h, k_h, D, H * k_h, k_h, D, H * q_h, q_h, D};
+}
+
 // c multiplies q . k into base-2 logits; v_mult multiplies O~ before it is
 // stored (1 for 16-bit K and V; for FP8, c carries K's descale and v_mult
 // is V's).
@@ -222,7 +236,7 @@ template <int D, int DT, bool CAUSAL, bool KV8>
 __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     float* __restrict__ part_o, float* __restrict__ part_ml, int Sq, int Sk, int n_split,
-    int chunk_keys, float c, float v_mult) {
+    int chunk_keys, float c, float v_mult, SkvStrides st) {
   using ST = SplitTile<D, KV8>;
   constexpr int RB = 1, Bc = ST::kBc, NKB = Bc / 32;
   constexpr int CPR = D / 8, TB = ST::kTileBytes, LPW = ST::kLoadsPerWave;
@@ -237,6 +251,7 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   const int split = blockIdx.x % n_split;
   const int qblk = blockIdx.x / n_split;
   const int bh = blockIdx.y + gridDim.y * blockIdx.z;
+  const int b = blockIdx.z, h = blockIdx.y;
   const int q0 = qblk * 32;
   const int row = q0 + l32;
   const int off = Sk - Sq;  // position of query 0 in the sequence
@@ -255,21 +270,33 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   for (int s = 0; s < NDS; ++s) {
     const int d0 = KV8 ? 32 * (s / 2) + 16 * hi + 8 * (s % 2) : 16 * s + 8 * hi;
     qf[0][s] = u32x4{0, 0, 0, 0};
-    if (row < Sq) qf[0][s] = *(const u32x4*)(q + ((size_t)bh * Sq + row) * D + d0);
+    if (row < Sq)
+      qf[0][s] = *(const u32x4*)(q + (size_t)(b * st.qb + h * st.qh) + (size_t)row * st.qs + d0);
   }
 
   constexpr int EB = KV8 ? 1 : 2;  // bytes per K or V element
-  const uint32_t head_bytes = (uint32_t)Sk * D * EB;
-  const unsigned char* k_head = (const unsigned char*)k + (size_t)bh * Sk * D * EB;
-  const unsigned char* v_head = (const unsigned char*)v + (size_t)bh * Sk * D * EB;
+  // K and V rows of this head, `k_rb` / `v_rb` bytes apart; buffers end
+  // with key Sk - 1, so loads of keys >= Sk return zero
+  const uint32_t k_rb = (uint32_t)st.ks * EB, v_rb = (uint32_t)st.vs * EB;
+  const uint32_t k_bytes = (uint32_t)Sk * k_rb, v_bytes = (uint32_t)Sk * v_rb;
+  const unsigned char* k_head = (const unsigned char*)k + (size_t)(b * st.kb + h * st.kh) * EB;
+  const unsigned char* v_head = (const unsigned char*)v + (size_t)(b * st.vb + h * st.vh) * EB;
   uint32_t k_off[LPW], v_off[LPW];
   if constexpr (KV8) {
-    tile_load_offsets8<D, LPW, false>(lane, k_off);
-    tile_load_offsets8<D, LPW, true>(lane, v_off);
+    tile_load_offsets8<D, LPW, false>(lane, k_rb, k_off);
+    tile_load_offsets8<D, LPW, true>(lane, v_rb, v_off);
   } else {
-    tile_load_offsets<D, LPW, false>(0, lane, k_off);
-    tile_load_offsets<D, LPW, true>(0, lane, v_off);
+    tile_load_offsets_strided<D, LPW, false>(0, lane, k_rb, k_off);
+    tile_load_offsets_strided<D, LPW, true>(0, lane, v_rb, v_off);
   }
+  auto load_k = [&](int t, uint32_t stage) {
+    load_tile_rsrc<LPW>(tile_rsrc_at(k_head, k_bytes, (uint32_t)t * (uint32_t)Bc * k_rb),
+                        smem + stage, 0, k_off);
+  };
+  auto load_v = [&](int t, uint32_t stage) {
+    load_tile_rsrc<LPW>(tile_rsrc_at(v_head, v_bytes, (uint32_t)t * (uint32_t)Bc * v_rb),
+                        smem + stage, 0, v_off);
+  };
   const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ swz_k<D>(l32)));
   const int vt_row = 4 * hi + (lane & 15) / 4;
   const int vt_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -292,8 +319,8 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   const int t_first = k_begin / Bc;
   const int n_t = k_end > k_begin ? (k_end - k_begin + Bc - 1) / Bc : 0;
   if (n_t > 0) {
-    load_tile<LPW, TB>(k_head, head_bytes, t_first, smem + kK0, 0, k_off);
-    load_tile<LPW, TB>(v_head, head_bytes, t_first, smem + kV0, 0, v_off);
+    load_k(t_first, kK0);
+    load_v(t_first, kV0);
   }
   for (int t = 0; t < n_t; ++t) {
     const uint32_t ks = (t & 1) ? kK1 : kK0, vs = (t & 1) ? kV1 : kV0;
@@ -301,8 +328,8 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
     // stages can take tile t + 1
     wait_vm_lgkm0<0>();
     if (t + 1 < n_t) {
-      load_tile<LPW, TB>(k_head, head_bytes, t_first + t + 1, smem + (ks ^ TB), 0, k_off);
-      load_tile<LPW, TB>(v_head, head_bytes, t_first + t + 1, smem + (vs ^ TB), 0, v_off);
+      load_k(t_first + t + 1, ks ^ TB);
+      load_v(t_first + t + 1, vs ^ TB);
     }
     f32x16 sc[RB][NKB];
     if constexpr (KV8)
@@ -365,7 +392,8 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
 template <int D, int DT>
 __global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int n_rows, int Sq, int n_split) {
+    float* __restrict__ lse, int n_rows, int H, int Sq, int n_split, long long ob, long long oh,
+    long long os) {
   using E = Elem<DT>;
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
@@ -425,7 +453,7 @@ __global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
     den += __shfl_xor(den, s);
   }
   const float inv = 1.0f / den;
-  uint16_t* orow = o + (size_t)r * D;
+  uint16_t* orow = o + (size_t)((bh / H) * ob + (bh % H) * oh + (long long)i * os);
 #pragma unroll
   for (int e = 0; e < PER; e += 2) {
     const uint32_t pk = E::pack2(num[e] * inv, (e + 1 < PER ? num[e + 1] : 0.f) * inv);
@@ -460,7 +488,7 @@ int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu, bool kv8) {
 template <int D, int DT, bool CAUSAL, bool KV8>
 hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                           int H, int Sq, int Sk, float scale, float k_mult, float v_mult,
-                          int n_split, void* ws, hipStream_t stream) {
+                          const SkvStrides& st, int n_split, void* ws, hipStream_t stream) {
   using ST = SplitTile<D, KV8>;
   // chunks of whole tiles; trailing splits that would be empty are dropped
   const int n_tiles = (Sk + ST::kBc - 1) / ST::kBc;
@@ -472,72 +500,92 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, 
   const dim3 grid((unsigned)(n_eff * n_qblk), (unsigned)H, (unsigned)B);
   fa2_splitkv_partial_kernel<D, DT, CAUSAL, KV8><<<grid, dim3(64), 0, stream>>>(
       (const uint16_t*)q, k, v, part_o, part_ml, Sq, Sk, n_eff, chunk_tiles * ST::kBc,
-      scale * kLog2e * k_mult, v_mult);
+      scale * kLog2e * k_mult, v_mult, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_rows = B * H * Sq;
   fa2_splitkv_combine_kernel<D, DT><<<dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
-      part_o, part_ml, (uint16_t*)o, lse, n_rows, Sq, n_eff);
+      part_o, part_ml, (uint16_t*)o, lse, n_rows, H, Sq, n_eff, st.ob, st.oh, st.os);
   return hipGetLastError();
 }
 
 template <int D, int DT, bool KV8>
 hipError_t launch_splitkv_causal(int causal, const void* q, const void* k, const void* v, void* o,
                                  float* lse, int B, int H, int Sq, int Sk, float scale,
-                                 float k_mult, float v_mult, int n_split, void* ws,
-                                 hipStream_t stream) {
+                                 float k_mult, float v_mult, const SkvStrides& st, int n_split,
+                                 void* ws, hipStream_t stream) {
   return causal ? launch_splitkv<D, DT, true, KV8>(q, k, v, o, lse, B, H, Sq, Sk, scale, k_mult,
-                                                   v_mult, n_split, ws, stream)
+                                                   v_mult, st, n_split, ws, stream)
                 : launch_splitkv<D, DT, false, KV8>(q, k, v, o, lse, B, H, Sq, Sk, scale, k_mult,
-                                                    v_mult, n_split, ws, stream);
+                                                    v_mult, st, n_split, ws, stream);
 }
 
 template <int D, bool KV8>
 hipError_t launch_splitkv_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                                 void* o, float* lse, int B, int H, int Sq, int Sk, float scale,
-                                float k_mult, float v_mult, int n_split, void* ws,
-                                hipStream_t stream) {
+                                float k_mult, float v_mult, const SkvStrides& st, int n_split,
+                                void* ws, hipStream_t stream) {
   return dtype == FA2_F16
              ? launch_splitkv_causal<D, FA2_F16, KV8>(causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
-                                                      k_mult, v_mult, n_split, ws, stream)
+                                                      k_mult, v_mult, st, n_split, ws, stream)
              : launch_splitkv_causal<D, FA2_BF16, KV8>(causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
-                                                       k_mult, v_mult, n_split, ws, stream);
+                                                       k_mult, v_mult, st, n_split, ws, stream);
 }
 
 template <bool KV8>
 hipError_t launch_splitkv_any(int D, int dtype, int causal, const void* q, const void* k,
                               const void* v, void* o, float* lse, int B, int H, int Sq, int Sk,
-                              float scale, float k_mult, float v_mult, int n_split, void* ws,
-                              hipStream_t stream) {
+                              float scale, float k_mult, float v_mult, const SkvStrides& st,
+                              int n_split, void* ws, hipStream_t stream) {
   switch (D) {
     case 64:
       return launch_splitkv_dtype<64, KV8>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
-                                           k_mult, v_mult, n_split, ws, stream);
+                                           k_mult, v_mult, st, n_split, ws, stream);
     case 128:
       return launch_splitkv_dtype<128, KV8>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
-                                            k_mult, v_mult, n_split, ws, stream);
+                                            k_mult, v_mult, st, n_split, ws, stream);
     default:
       return launch_splitkv_dtype<256, KV8>(dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
-                                            k_mult, v_mult, n_split, ws, stream);
+                                            k_mult, v_mult, st, n_split, ws, stream);
   }
 }
 
-// Checks shared by the two split-KV entry points, in the documented order,
-// and the launch. kv_elem_bytes: 2 for 16-bit K and V, 1 for FP8.
+// Checks shared by the split-KV entry points, in the documented order, and
+// the launch. kv_elem_bytes: 2 for 16-bit K and V, 1 for FP8. strides:
+// nullptr for contiguous tensors, else 12 element strides.
 int splitkv_call(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int Sq, int Sk, int D, int causal, float scale, int dtype, float k_descale,
-                 float v_descale, int kv_elem_bytes, int n_split, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 int Sq, int Sk, int D, const long long* strides, int causal, float scale,
+                 int dtype, float k_descale, float v_descale, int kv_elem_bytes, int n_split,
+                 void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || B > 65535 || H > 65535 || n_split < 0)
     return FA2_ERR_SHAPE;
   if (causal && Sq > Sk) return FA2_ERR_SHAPE;  // the first queries would have no key
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
   if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
+  const SkvStrides st =
+      strides ? SkvStrides{strides[0], strides[1], strides[2], strides[3], strides[4],
+                           strides[5], strides[6], strides[7], strides[8], strides[9],
+                           strides[10], strides[11]}
+              : contiguous_strides(H, Sq, Sk, D);
+  if (strides) {
+    // strides in [0, 2^40]; rows 16-byte aligned (8 elements of q and o, and
+    // of 16-bit K and V; 16 FP8 codes); sequence strides at least D
+    for (int i = 0; i < 12; ++i) {
+      const long long x = strides[i];
+      const bool kv = i >= 3 && i < 9;
+      const long long align = kv && kv_elem_bytes == 1 ? 16 : 8;
+      if (x < 0 || x > (1LL << 40) || x % align) return FA2_ERR_STRIDE;
+      if (i % 3 == 2 && x < D) return FA2_ERR_STRIDE;
+    }
+  }
   // one head of K or V, plus a tile past its end, within 32-bit byte offsets;
   // query rows of the whole call indexed in 32 bits
-  if (((long long)Sk + 256) * D * kv_elem_bytes > (long long)INT32_MAX) return FA2_ERR_SHAPE;
+  if (((long long)Sk + 256) * st.ks * kv_elem_bytes > (long long)INT32_MAX ||
+      ((long long)Sk + 256) * st.vs * kv_elem_bytes > (long long)INT32_MAX)
+    return FA2_ERR_SHAPE;
   if ((long long)B * H * Sq > (long long)INT32_MAX / 4) return FA2_ERR_SHAPE;
+  if (strides && !rows_disjoint(B, H, Sq, D, st.ob, st.oh, st.os)) return FA2_ERR_STRIDE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
   if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
@@ -557,15 +605,18 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
   if (n_split > 65536) return FA2_ERR_SHAPE;
   const size_t need = splitkv_workspace_bytes(B, H, Sq, D, n_split);
   if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return FA2_ERR_WORKSPACE;
-  const size_t q_bytes = (size_t)B * H * Sq * D * 2;
-  const size_t kv_bytes = (size_t)B * H * Sk * D * kv_elem_bytes;
+  // overlap, by the byte range each tensor spans
+  const size_t q_bytes = extent_bytes(B, H, Sq, D, st.qb, st.qh, st.qs, 2);
+  const size_t k_bytes = extent_bytes(B, H, Sk, D, st.kb, st.kh, st.ks, kv_elem_bytes);
+  const size_t v_bytes = extent_bytes(B, H, Sk, D, st.vb, st.vh, st.vs, kv_elem_bytes);
+  const size_t o_bytes = extent_bytes(B, H, Sq, D, st.ob, st.oh, st.os, 2);
   const size_t lse_bytes = (size_t)B * H * Sq * sizeof(float);
-  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) ||
-      overlaps(o, q_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, q, q_bytes) ||
-      overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
-      overlaps(lse, lse_bytes, o, q_bytes) || overlaps(workspace, need, q, q_bytes) ||
-      overlaps(workspace, need, k, kv_bytes) || overlaps(workspace, need, v, kv_bytes) ||
-      overlaps(workspace, need, o, q_bytes) || overlaps(workspace, need, lse, lse_bytes))
+  if (overlaps(o, o_bytes, q, q_bytes) || overlaps(o, o_bytes, k, k_bytes) ||
+      overlaps(o, o_bytes, v, v_bytes) || overlaps(lse, lse_bytes, q, q_bytes) ||
+      overlaps(lse, lse_bytes, k, k_bytes) || overlaps(lse, lse_bytes, v, v_bytes) ||
+      overlaps(lse, lse_bytes, o, o_bytes) || overlaps(workspace, need, q, q_bytes) ||
+      overlaps(workspace, need, k, k_bytes) || overlaps(workspace, need, v, v_bytes) ||
+      overlaps(workspace, need, o, o_bytes) || overlaps(workspace, need, lse, lse_bytes))
     return FA2_ERR_ALIAS;
   if (!device_checked) {
     const int dev = check_device(&n_cu);
@@ -573,13 +624,13 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
   }
 
   (void)hipGetLastError();
-  const hipStream_t st = (hipStream_t)stream;
+  const hipStream_t hs = (hipStream_t)stream;
   const hipError_t err =
       kv_elem_bytes == 1
           ? launch_splitkv_any<true>(D, dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale,
-                                     k_descale, v_descale, n_split, workspace, st)
+                                     k_descale, v_descale, st, n_split, workspace, hs)
           : launch_splitkv_any<false>(D, dtype, causal, q, k, v, o, lse, B, H, Sq, Sk, scale, 1.f,
-                                      1.f, n_split, workspace, st);
+                                      1.f, st, n_split, workspace, hs);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 
@@ -615,8 +666,8 @@ extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void
                                int B, int H, int Sq, int Sk, int D, int causal, float scale,
                                int dtype, int n_split, void* workspace, size_t workspace_bytes,
                                void* stream) {
-  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype, 1.f, 1.f, 2, n_split,
-                      workspace, workspace_bytes, stream);
+  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, nullptr, causal, scale, dtype, 1.f, 1.f, 2,
+                      n_split, workspace, workspace_bytes, stream);
 }
 
 extern "C" int fa2_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o,
@@ -624,6 +675,19 @@ extern "C" int fa2_fwd_splitkv_fp8(const void* q, const void* k, const void* v, 
                                    float scale, float k_descale, float v_descale, int dtype,
                                    int n_split, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype, k_descale, v_descale,
-                      1, n_split, workspace, workspace_bytes, stream);
+  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, nullptr, causal, scale, dtype, k_descale,
+                      v_descale, 1, n_split, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa2_fwd_splitkv_strided(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int H, int Sq, int Sk, int D,
+                                       const long long* strides, int causal, float scale,
+                                       int dtype, int kv_fp8, float k_descale, float v_descale,
+                                       int n_split, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!q || !k || !v || !o || !lse || !strides) return FA2_ERR_NULL;
+  if (kv_fp8 != 0 && kv_fp8 != 1) return FA2_ERR_DTYPE;
+  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, strides, causal, scale, dtype,
+                      kv_fp8 ? k_descale : 1.f, kv_fp8 ? v_descale : 1.f, kv_fp8 ? 1 : 2, n_split,
+                      workspace, workspace_bytes, stream);
 }

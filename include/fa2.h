@@ -194,6 +194,32 @@ int fa2_fwd_splitkv_fp8(const void *q, const void *k, const void *v, void *o, fl
                         float k_descale, float v_descale, int dtype, int n_split,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * fa2_fwd_splitkv_strided -- fa2_fwd_splitkv (kv_fp8 = 0) or
+ * fa2_fwd_splitkv_fp8 (kv_fp8 = 1, with k_descale and v_descale) on tensors
+ * with arbitrary strides, such as a KV cache allocated for a maximum length
+ * and read up to the current one, or kept as (B, S, H, D).
+ *
+ * strides  host pointer to 12 element strides: batch, head and sequence of
+ *          q, then of k, v and o (FP8 K and V count bytes). Each stride is
+ *          in [0, 2^40]; rows are 16-byte aligned (multiples of 8 elements
+ *          for 16-bit tensors, of 16 for FP8 K and V); each sequence stride
+ *          is >= D; o's rows must be disjoint. K and V may repeat one head
+ *          (head stride 0).
+ * lse      contiguous (B, H, Sq) floats. One head of K and of V must span
+ *          under 2 GiB: (Sk + 256) * sequence stride * element bytes.
+ * The workspace, the other arguments and the result are those of the
+ * contiguous calls, which the strided call reproduces bit for bit.
+ * FA2_ERR_STRIDE for bad strides, FA2_ERR_DTYPE for kv_fp8 other than 0 or
+ * 1, otherwise the codes of fa2_fwd_splitkv; overlap is judged on the byte
+ * range each tensor spans.
+ */
+int fa2_fwd_splitkv_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Sq, int Sk, int D, const long long *strides,
+                            int causal, float scale, int dtype, int kv_fp8, float k_descale,
+                            float v_descale, int n_split, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace fa2_fwd_splitkv and fa2_fwd_splitkv_fp8 need for these
  * sizes and n_split; n_split = 0 gives enough for the default split count
  * of either. 0 for invalid sizes or head dims. */

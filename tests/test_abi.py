@@ -345,6 +345,55 @@ def test_splitkv_fp8_kv_extent_is_one_byte_per_element(lib):
     assert _call_splitkv_fp8(o=KS + _SK * _D - 16) == fa.FA2_ERR_ALIAS
 
 
+_SKV_CONTIG = [_SQ * _D, _SQ * _D, _D, _SK * _D, _SK * _D, _D, _SK * _D, _SK * _D, _D,
+               _SQ * _D, _SQ * _D, _D]
+
+
+def _call_splitkv_strided(**kw):
+    args = dict(q=QS, k=KS, v=VS, o=OS, lse=LS, B=1, H=1, Sq=_SQ, Sk=_SK, D=_D,
+                strides=list(_SKV_CONTIG), causal=0, scale=0.125, dtype=fa.FA2_F16, kv_fp8=0,
+                k_descale=1.0, v_descale=1.0, n_split=4, workspace=WS,
+                workspace_bytes=_ws_bytes(4), stream=None)
+    args.update(kw)
+    return fa.fa2_fwd_splitkv_strided(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(strides=None), fa.FA2_ERR_NULL),
+    (dict(q=None), fa.FA2_ERR_NULL),
+    (dict(kv_fp8=2), fa.FA2_ERR_DTYPE),
+    (dict(strides=_with(_SKV_CONTIG, s5=32)), fa.FA2_ERR_STRIDE),       # k rows overlap (< D)
+    (dict(strides=_with(_SKV_CONTIG, s0=4)), fa.FA2_ERR_STRIDE),        # q rows not 16-byte aligned
+    (dict(strides=_with(_SKV_CONTIG, s5=72), kv_fp8=1, k_descale=0.1,
+          v_descale=0.1), fa.FA2_ERR_STRIDE),                            # FP8 rows of 72 bytes
+    (dict(strides=_with(_SKV_CONTIG, s10=0, s9=0), H=2, B=2), fa.FA2_ERR_STRIDE),  # o rows shared
+    (dict(strides=_with(_SKV_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),   # a K head past 2 GiB
+    (dict(kv_fp8=1, k_descale=0.0), fa.FA2_ERR_SCALE),
+    (dict(o=KS + 64), fa.FA2_ERR_ALIAS),
+])
+def test_splitkv_strided_validation_status(lib, kw, status):
+    assert _call_splitkv_strided(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(kv_fp8=1, k_descale=0.01, v_descale=0.02),
+    # a cache of 4 * Sk rows read up to Sk, (B, S, H, D)-style head stride D
+    dict(strides=_with(_SKV_CONTIG, s3=4 * _SK * _D, s4=_D, s5=2 * _D, s6=4 * _SK * _D, s7=_D,
+                       s8=2 * _D), H=2),
+], ids=["contiguous", "fp8", "cache_view"])
+def test_splitkv_strided_valid_calls_reach_the_device_check(lib, kw):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    if kw.get("H") == 2:
+        # two heads: o and lse grow, the workspace too
+        kw = dict(kw, workspace_bytes=fa.fa2_splitkv_workspace_bytes(1, 2, _SQ, _SK, _D, 4),
+                  strides=[2 * _SQ * _D, _SQ * _D, _D] + kw["strides"][3:9]
+                  + [2 * _SQ * _D, _SQ * _D, _D])
+    assert _call_splitkv_strided(**kw) == fa.FA2_ERR_NO_DEVICE
+
+
 def test_splitkv_no_device_status_without_gpu(lib):
     import torch
     if torch.cuda.device_count() > 0:
