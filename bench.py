@@ -6,7 +6,7 @@ resident in HBM). Default workload: B=2, H=16, S=8192, D=128, fp16, causal.
 Prints one JSON line on stdout; diagnostics go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-    python bench.py --table PATH      # every benchmark shape, one line each
+    python bench.py --table PATH      # every benchmark shape: fa2_fwd, and fa2_fwd_balanced where it splits
     python bench.py --decode-table PATH   # split-KV decode shapes, GB/s
     python bench.py --layer           # attention layer it/s and peak memory
 
@@ -74,7 +74,9 @@ def read_traffic(workload_name: str):
         return None
 
 
-def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0):
+def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0, balanced: bool = False):
+    """Per-launch HIP-event durations of fa2_fwd on w (balanced: of
+    fa2_fwd_balanced, both its kernels when it splits the keys)."""
     import torch
 
     import flashattention_tiled_amd as fa
@@ -90,9 +92,13 @@ def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0):
     lib = fa.load_library()
     args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
             w.B, w.H, w.S, w.D, int(w.causal), float(w.scale), dtype, stream.cuda_stream)
+    if balanced:
+        need = fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, int(w.causal))
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+        args = args[:9] + (None,) + args[9:12] + (ws.data_ptr(), need, stream.cuda_stream)
 
     def launch():
-        st = lib.fa2_fwd(*args)
+        st = (lib.fa2_fwd_balanced if balanced else lib.fa2_fwd)(*args)
         if st != 0:
             raise fa.FA2Error(st, fa.fa2_status_string(st))
 
@@ -331,20 +337,28 @@ def stats_line(w, r):
 def run_table(path: str, steps: int, warmup: int):
     import workloads as wl
 
+    import flashattention_tiled_amd as fa
+
     rows = []
     for w in wl.ALL:
-        r = time_gpu(w, steps, warmup, warmup_min_s=0.3)
-        avg, med = stats_line(w, r)
-        tf = w.flops / (med * 1e-3) / 1e12
-        gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9
-        line = (f"{w.name},{w.B},{w.H},{w.S},{w.D},{w.dtype},{int(w.causal)},"
-                f"{med:.4f},{avg:.4f},{min(r['durs_ms']):.4f},{tf:.1f},"
-                f"{100 * tf / PEAK_TFLOPS:.2f},{gbs:.1f}")
-        log(line)
-        rows.append(line)
-        del r
+        # fa2_fwd, and fa2_fwd_balanced where it splits the keys of this shape
+        entries = ["fa2_fwd"]
+        if fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, int(w.causal)) > 0:
+            entries.append("fa2_fwd_balanced")
+        for entry in entries:
+            r = time_gpu(w, steps, warmup, warmup_min_s=0.3, balanced=entry != "fa2_fwd")
+            avg, med = stats_line(w, r)
+            tf = w.flops / (med * 1e-3) / 1e12
+            gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9
+            line = (f"{w.name},{entry},{w.B},{w.H},{w.S},{w.D},{w.dtype},{int(w.causal)},"
+                    f"{med:.4f},{avg:.4f},{min(r['durs_ms']):.4f},{tf:.1f},"
+                    f"{100 * tf / PEAK_TFLOPS:.2f},{gbs:.1f}")
+            log(line)
+            rows.append(line)
+            del r
     with open(path, "w") as f:
-        f.write("workload,B,H,S,D,dtype,causal,ms_median,ms_avg,ms_min,tflops,pct_peak,alg_GBps\n")
+        f.write("workload,entry,B,H,S,D,dtype,causal,ms_median,ms_avg,ms_min,tflops,pct_peak,"
+                "alg_GBps\n")
         f.write("\n".join(rows) + "\n")
 
 

@@ -10,6 +10,9 @@ C entry points, re-exported under the same names:
     fa2_fwd(q, k, v, o, lse, B, H, S, D, causal, scale, dtype, stream) -> int
     fa2_fwd_strided(q, k, v, o, lse, B, H, S, D, strides, causal, scale, dtype,
                     stream) -> int   (strides: 12 element strides)
+    fa2_fwd_balanced(q, k, v, o, lse, B, H, S, D, strides, causal, scale, dtype,
+                     workspace, workspace_bytes, stream) -> int   (strides or None)
+    fa2_fwd_balanced_workspace_bytes(B, H, S, D, causal) -> int
     fa2_supported(D, dtype) -> int
     fa2_status_string(status) -> str
     fa2_rows_per_workgroup(D) -> int
@@ -25,7 +28,8 @@ C entry points, re-exported under the same names:
     fa2_splitkv_splits(B, H, Sq, Sk) -> int
     fa2_splitkv_splits_fp8(B, H, Sq, Sk) -> int
 plus the tensor-level conveniences ``attention(q, k, v, causal, scale)`` (any
-layout whose head dim is contiguous) and
+layout whose head dim is contiguous; the key-split fa2_fwd_balanced when the
+library plans a split for the shape) and
 ``attention_splitkv(q, k, v, causal, scale, n_split)`` (Sq queries against Sk
 cached keys).
 """
@@ -56,7 +60,8 @@ FA2_ERR_ALIAS = 9
 FA2_ERR_WORKSPACE = 10
 FA2_ERR_STRIDE = 11
 
-EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_supported", "fa2_status_string",
+EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_fwd_balanced",
+                    "fa2_fwd_balanced_workspace_bytes", "fa2_supported", "fa2_status_string",
                     "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_fwd_splitkv_fp8",
                     "fa2_fwd_splitkv_strided",
                     "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits",
@@ -113,13 +118,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa2_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i,
                                     ctypes.POINTER(ctypes.c_longlong), i, f, i, vp]
     lib.fa2_fwd_strided.restype = i
+    sz = ctypes.c_size_t
+    lib.fa2_fwd_balanced.argtypes = [vp, vp, vp, vp, vp, i, i, i, i,
+                                     ctypes.POINTER(ctypes.c_longlong), i, f, i, vp, sz, vp]
+    lib.fa2_fwd_balanced.restype = i
+    lib.fa2_fwd_balanced_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa2_fwd_balanced_workspace_bytes.restype = sz
     lib.fa2_supported.argtypes = [i, i]
     lib.fa2_supported.restype = i
     lib.fa2_status_string.argtypes = [i]
     lib.fa2_status_string.restype = ctypes.c_char_p
     lib.fa2_rows_per_workgroup.argtypes = [i]
     lib.fa2_rows_per_workgroup.restype = i
-    sz = ctypes.c_size_t
     lib.fa2_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa2_fwd_splitkv.restype = i
     lib.fa2_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, i, i, vp, sz,
@@ -153,6 +163,21 @@ def fa2_fwd_strided(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S:
     st = None if strides is None else (ctypes.c_longlong * 12)(*[int(x) for x in strides])
     return int(load_library().fa2_fwd_strided(q, k, v, o, lse, B, H, S, D, st, int(causal),
                                               float(scale), int(dtype), stream))
+
+
+def fa2_fwd_balanced(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+                     strides, causal: int, scale: float, dtype: int, workspace: int,
+                     workspace_bytes: int, stream: int) -> int:
+    """Direct call of the key-split entry point; `strides` is None
+    (contiguous tensors) or 12 element strides. Returns the status."""
+    st = None if strides is None else (ctypes.c_longlong * 12)(*[int(x) for x in strides])
+    return int(load_library().fa2_fwd_balanced(q, k, v, o, lse, B, H, S, D, st, int(causal),
+                                               float(scale), int(dtype), workspace,
+                                               int(workspace_bytes), stream))
+
+
+def fa2_fwd_balanced_workspace_bytes(B: int, H: int, S: int, D: int, causal: int) -> int:
+    return int(load_library().fa2_fwd_balanced_workspace_bytes(B, H, S, D, int(causal)))
 
 
 def fa2_supported(D: int, dtype: int) -> int:
@@ -222,13 +247,17 @@ def _dtype_code(t):
 
 
 def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-              stream=None):
+              stream=None, balanced: bool = True, workspace=None):
     """O, lse = softmax(scale * q k^T [causal]) v for (B, H, S, D) CUDA tensors.
 
     q, k, v: torch tensors on one GPU, fp16 or bf16, same shape, each with a
     contiguous last (head) dim; other strides are free (e.g. the (B, H, S, D)
     views of a packed (B, S, 3, H, D) projection). Contiguous tensors go to
-    fa2_fwd, others to fa2_fwd_strided. scale defaults to 1/sqrt(D). Returns
+    fa2_fwd, others to fa2_fwd_strided; with `balanced` (the default), shapes
+    whose grid is too small to keep the GPU busy to the end go to
+    fa2_fwd_balanced instead, with `workspace` (a CUDA uint8 tensor of at
+    least fa2_fwd_balanced_workspace_bytes bytes) or one allocated with
+    torch. scale defaults to 1/sqrt(D). Returns
     (o, lse): o of q's shape (a new contiguous tensor unless `out`, which may
     be any view with a contiguous last dim, is given), lse (B, H, S) float32
     (natural-log logsumexp per row). Runs on `stream` (default: torch's
@@ -261,7 +290,17 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         stream = torch.cuda.current_stream(q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, out))
     with torch.cuda.device(q.device):
-        if contiguous:
+        need = fa2_fwd_balanced_workspace_bytes(B, H, S, D, int(bool(causal))) if balanced else 0
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+            strides = None if contiguous else [x for t in (q, k, v, out) for x in t.stride()[:3]]
+            status = fa2_fwd_balanced(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), B, H, S, D, strides, int(bool(causal)),
+                                      float(scale), _dtype_code(q), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(),
+                                      stream.cuda_stream)
+        elif contiguous:
             status = fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr(), B, H, S, D, int(bool(causal)), float(scale),
                              _dtype_code(q), stream.cuda_stream)

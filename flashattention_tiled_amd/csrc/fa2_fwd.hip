@@ -38,8 +38,11 @@
 // The matrix-core formulation, lane layouts and LDS staging shared with
 // the split-KV kernels are described in fa2_tile.h.
 
+#include <algorithm>
+
 #include "fa2_tile.h"
 #include "fa2_host.h"
+#include "fa2_combine.h"
 
 using fa2_host::check_device;
 using fa2_host::extent_bytes;
@@ -327,11 +330,55 @@ struct Strides {
   long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
 };
 
+// The key split of a launch (ct = 0: none). When there are too few query
+// tiles to keep every compute unit busy to the end -- under causal masking
+// the last tile of a head has twice the average's keys -- the keys of a
+// query tile are cut into chunks of ct key tiles that run as separate
+// workgroups, and rows whose tile has more than one chunk leave the chunk
+// partials of fa2_combine.h for the merge. Causal: chunks are m query tiles'
+// worth of keys (ct = m B_r / B_c), so chunk c of tile qt exists iff
+// c <= qt / m and starts at or before the tile's first row, and the rows
+// from row0 = m B_r on are merged. Non-causal: every tile has n_split
+// chunks and every row is merged (row0 = 0).
+struct KeySplit {
+  int ct, m, n_qt, n_split, row0;
+  float* part_o;
+  float* part_ml;
+};
+
+// Work item u of one (b, h) under the causal key split, in launch order:
+// first the chunks of a full ct tiles, chunk by chunk, then the shorter
+// last chunks, longest first (the last chunk of tile qt = c m + r holds
+// r + 1 query tiles' worth of keys), so that compute units take the long
+// items first and the short ones fill in at the end.
+__host__ __device__ __forceinline__ void causal_split_item(int u, int n_qt, int m, int& qt, int& c) {
+  for (c = 0;; ++c) {
+    const int first = c * m + m - 1;  // the first tile with a full chunk c
+    if (first >= n_qt) break;
+    if (u < n_qt - first) {
+      qt = first + u;
+      return;
+    }
+    u -= n_qt - first;
+  }
+  for (int r = m - 2; r >= 0; --r) {
+    const int p = r < n_qt ? (n_qt - 1 - r) / m + 1 : 0;  // tiles c m + r < n_qt
+    if (u < p) {
+      c = u;
+      qt = c * m + r;
+      return;
+    }
+    u -= p;
+  }
+  qt = 0;  // not reached: u is below the item count
+  c = 0;
+}
+
 template <int D, int DT, bool CAUSAL, bool STRIDED, bool LONG>
 __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesPerSimd)) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, float c /* scale * log2(e) */, int pair_split, Strides st) {
+    int S, float c /* scale * log2(e) */, int pair_split, Strides st, KeySplit ks) {
   using SH = Shape<D, LONG>;
   using E = Elem<DT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
@@ -357,12 +404,27 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   // the workgroups from pair_split on take the query tiles in ascending
   // order instead, so that the second workgroup a compute unit receives is
   // a light tile beside its heavy first one.
-  const int n_qt = gridDim.x;
+  // Under a key split the grid's x dimension runs over work items instead,
+  // each one key chunk (of ct tiles from tile t0) of one query tile.
   const int n_bh = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int bh = lin % n_bh;
-  const int qt = (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh
-                                                       : n_qt - 1 - lin / n_bh;
+  int qt, chunk = 0;
+  if (ks.ct > 0) {
+    const int u = lin / n_bh;
+    if constexpr (CAUSAL) {
+      causal_split_item(u, ks.n_qt, ks.m, qt, chunk);
+    } else {
+      chunk = u / ks.n_qt;
+      qt = u - chunk * ks.n_qt;
+    }
+  } else {
+    const int n_qt = gridDim.x;
+    qt = (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh : n_qt - 1 - lin / n_bh;
+  }
+  const int t0 = chunk * ks.ct;  // first key tile
+  // chunks of this query tile (more than one: the rows leave partials)
+  const int n_chunks = ks.ct == 0 ? 1 : CAUSAL ? qt / ks.m + 1 : ks.n_split;
   const int q0 = qt * Br;
   const int wave_row0 = q0 + wave * SH::kRowsPerWave;
 
@@ -453,11 +515,14 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   }
 
   const int kv_end = CAUSAL ? min(q0 + Br, S) : S;
-  const int n_tiles = (kv_end + Bc - 1) / Bc;  // tiles the workgroup loads
+  const int t_all = (kv_end + Bc - 1) / Bc;
+  const int t_stop = ks.ct > 0 ? min(t_all, t0 + ks.ct) : t_all;
+  const int n_tiles = t_stop - t0;  // tiles the workgroup loads, from t0
   // tiles this wave computes (under causal masking the later tiles of the
-  // workgroup lie wholly above this wave's rows)
+  // workgroup lie wholly above this wave's rows); at least one, as t0 B_c
+  // is at most the tile's first row
   const int n_act =
-      CAUSAL ? min(n_tiles, (wave_row0 + SH::kRowsPerWave + Bc - 1) / Bc) : n_tiles;
+      CAUSAL ? min(t_stop, (wave_row0 + SH::kRowsPerWave + Bc - 1) / Bc) - t0 : n_tiles;
 
   // Software pipeline. Iteration j computes the scores of tile j + 1 on the
   // matrix cores while the vector unit turns tile j's scores into P, then the
@@ -466,19 +531,19 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   // tile j) has landed, and after the barrier every wave is done with
   // iteration j - 1, so K of tile j + 2 goes into tile j's K stage and V of
   // tile j + 1 into tile j - 1's V stage.
-  load_tile_rsrc<LPW>(k_tile(k_bytes, 0), smem + kK0, wave, k_off);
-  load_tile_rsrc<LPW>(v_tile(v_bytes, 0), smem + kV0, wave, v_off);
-  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(k_bytes, 1), smem + kK1, wave, k_off);
+  load_tile_rsrc<LPW>(k_tile(k_bytes, t0), smem + kK0, wave, k_off);
+  load_tile_rsrc<LPW>(v_tile(v_bytes, t0), smem + kV0, wave, v_off);
+  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(k_bytes, t0 + 1), smem + kK1, wave, k_off);
 
   f32x16 s_a[RB][NKB], s_b[RB][NKB];
   float ce_a[RB], ce_b[RB];
   wait_vm_lgkm0<0>();
   workgroup_barrier();
   if (n_act > 0) {
-    // m starts at the row max of tile 0, which holds an unmasked key for
-    // every row (key 0), so m is finite from here on
+    // m starts at the row max of tile t0, which holds an unmasked key for
+    // every row (key t0 B_c <= q0), so m is finite from here on
     tile_scores<D, DT, RB, NKB>(smem, kK0, k_lane, qf, s_a);
-    tile_mask<RB, NKB, CAUSAL>(s_a, 0, wave_row0, S, c, l32, hi, ce_a);
+    tile_mask<RB, NKB, CAUSAL>(s_a, t0 * Bc, wave_row0, S, c, l32, hi, ce_a);
     tile_max<RB, NKB>(s_a, ce_a, m_run);
   }
 
@@ -497,8 +562,8 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     // K of tile j + 2 and V of tile j + 1; a tile past the workgroup's last
     // gets a zero-length buffer, so its loads only write zeros to a free stage
     const StepLoads<LPW> ld{
-        k_tile(j + 2 < n_tiles ? k_bytes : 0u, j + 2),
-        v_tile(j + 1 < n_tiles ? v_bytes : 0u, j + 1),
+        k_tile(j + 2 < n_tiles ? k_bytes : 0u, t0 + j + 2),
+        v_tile(j + 1 < n_tiles ? v_bytes : 0u, t0 + j + 1),
         smem + k_free, smem + v_free, k_off, v_off, wave};
     if (j < n_act) {
       // scores of tile j + 1 || probabilities of tile j, then P V of tile j
@@ -507,8 +572,8 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
       pipeline_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery>(
           ld, smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt, acc_o);
       if (j + 1 < n_act) {
-        if (tile_needs_mask<RB, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S)) {
-          tile_mask<RB, NKB, CAUSAL>(nxt, (j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
+        if (tile_needs_mask<RB, NKB, CAUSAL>((t0 + j + 1) * Bc, wave_row0, S)) {
+          tile_mask<RB, NKB, CAUSAL>(nxt, (t0 + j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
         } else {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) ce_nxt[rb] = c;
@@ -528,13 +593,30 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   wait_vm_lgkm0<0>();
 
   // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, and
-  // lse = ln2 (m + log2 l) from the unrounded sum.
+  // lse = ln2 (m + log2 l) from the unrounded sum; or, for one chunk of a
+  // split tile, the chunk's partial O~, m, l and l' for the merge.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = wave_row0 + 32 * rb + l32;
     const float l_tot = xor32_sum(l_run[rb]);
     const float l_o = xor32_sum(l_rnd[rb]);
-    if (row < S) {
+    if (row < S && n_chunks > 1) {
+      const size_t prow =
+          ((size_t)bh * ks.n_split + chunk) * (size_t)(S - ks.row0) + (size_t)(row - ks.row0);
+      float* po = ks.part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(float4*)(po + 32 * db + 8 * g + 4 * hi) =
+              float4{acc_o[rb][db][4 * g], acc_o[rb][db][4 * g + 1], acc_o[rb][db][4 * g + 2],
+                     acc_o[rb][db][4 * g + 3]};
+      if (hi == 0) {
+        ks.part_ml[prow * 3 + 0] = m_run[rb];
+        ks.part_ml[prow * 3 + 1] = l_tot;
+        ks.part_ml[prow * 3 + 2] = l_o;
+      }
+    } else if (row < S) {
       const float inv = 1.0f / l_o;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -550,60 +632,193 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
 }
 
 // Launch the kernel over (B, H, S); `st` gives the strides of a strided call
-// (nullptr: contiguous tensors).
+// (nullptr: contiguous tensors), `ks` a key split (ct = 0: none), whose
+// merge follows on the same stream.
 template <int D, int DT, bool CAUSAL, bool LONG>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                  int H, int S, float scale, const Strides* st, int n_cu, hipStream_t stream) {
+                  int H, int S, float scale, const Strides* st, const KeySplit& ks, int n_cu,
+                  hipStream_t stream) {
   using SH = Shape<D, LONG>;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
-  const dim3 grid((unsigned)n_qt, (unsigned)H, (unsigned)B);
+  // work items per (b, h): query tiles, or their key chunks under a split
+  int n_x = n_qt;
+  if (ks.ct > 0) {
+    if (CAUSAL) {
+      n_x = 0;
+      for (int t = 0; t < n_qt; ++t) n_x += t / ks.m + 1;
+    } else {
+      n_x = n_qt * ks.n_split;
+    }
+  }
+  const dim3 grid((unsigned)n_x, (unsigned)H, (unsigned)B);
   const dim3 block(SH::kThreads);
   // workgroups resident per compute unit: the register budget allows
   // kWavesPerSimd waves per SIMD, i.e. that many 4-wave workgroups
   const long long slots = (long long)n_cu * Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves;
   const long long n_wg = (long long)n_qt * H * B;
-  const int pair_split =
-      (CAUSAL && n_qt > 1 && n_wg <= slots) ? (int)(((n_qt + 1) / 2) * (long long)H * B) : 0;
+  const int pair_split = (CAUSAL && ks.ct == 0 && n_qt > 1 && n_wg <= slots)
+                             ? (int)(((n_qt + 1) / 2) * (long long)H * B)
+                             : 0;
+  const Strides cs{(long long)H * S * D, (long long)S * D, D, (long long)H * S * D,
+                   (long long)S * D,     D,                 (long long)H * S * D, (long long)S * D,
+                   D,                    (long long)H * S * D, (long long)S * D, D};
   if (st)
     fa2_fwd_kernel<D, DT, CAUSAL, true, LONG><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
-        scale * kLog2e, pair_split, *st);
+        scale * kLog2e, pair_split, *st, ks);
   else
     fa2_fwd_kernel<D, DT, CAUSAL, false, LONG><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
-        scale * kLog2e, pair_split, Strides{});
-  return hipGetLastError();
+        scale * kLog2e, pair_split, cs, ks);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ks.ct == 0) return err;
+  const Strides& os = st ? *st : cs;
+  return launch_combine<D, DT>(ks.part_o, ks.part_ml, o, lse, B * H, H, S, ks.row0,
+                               CAUSAL ? ks.row0 : 0, ks.n_split, os.ob, os.oh, os.os, stream);
 }
 
 template <int D, bool LONG>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                         void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
-                        int n_cu, hipStream_t stream) {
+                        const KeySplit& ks, int n_cu, hipStream_t stream) {
   if (dtype == FA2_F16)
-    return causal ? launch<D, FA2_F16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
-                  : launch<D, FA2_F16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu,
+    return causal ? launch<D, FA2_F16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
+                                                   stream)
+                  : launch<D, FA2_F16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
                                                     stream);
-  return causal ? launch<D, FA2_BF16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu, stream)
-                : launch<D, FA2_BF16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, n_cu,
+  return causal ? launch<D, FA2_BF16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
+                                                  stream)
+                : launch<D, FA2_BF16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
                                                    stream);
+}
+
+// Shortest key chunk, in keys.
+constexpr int kSplitMinChunkKeys = 512;
+// The cost model a split must win by kSplitMargin, from measurements on
+// MI355X. A compute unit computes about kCuFlopsAlone[D] FLOP/s for a
+// workgroup it holds alone (one wave per SIMD) and kCuFlopsFull[D] when
+// full, shared among its workgroups (index 0, 1, 2: D = 64, 128, 256). The
+// merge reads the partials back and writes O at about kMergeBytesPerSec
+// after a fixed kMergeFixedSec, and writing the partials costs the prefill
+// kernel about their bytes at kPartialWriteBytesPerSec.
+constexpr double kCuFlopsAlone[3] = {2.3e12, 3.7e12, 3.9e12};
+constexpr double kCuFlopsFull[3] = {3.3e12, 3.9e12, 3.9e12};
+constexpr double kMergeBytesPerSec = 3.0e12;
+constexpr double kPartialWriteBytesPerSec = 6.0e12;
+constexpr double kMergeFixedSec = 3.0e-6;
+constexpr double kSplitMargin = 1.5;
+
+// The key split for a launch of (B, H, S) on n_cu compute units (ct = 0:
+// none; the buffers are left unset). Causal grids that leave compute units
+// with a single workgroup (one wave per SIMD) -- at most half the
+// workgroups the GPU holds at once, or one round where a unit holds just
+// one -- end on their longest workgroup, the last query tile of a head
+// with all S keys, twice the average. (Causal grids of up to one round on
+// units that hold two are kept balanced per unit by the kernel's
+// heavy-light tile order, and a split does not speed them up.) Non-causal
+// grids are even and only gain where at least half the compute units would
+// otherwise idle. The split cuts every tile's keys into chunks: causal, of
+// about T / slots key tiles, T being all the tiles of the launch;
+// non-causal, into n_cu / tiles chunks per tile, one per compute unit. A
+// launch takes at least its longest
+// workgroup's tiles (unsplit: alone on its compute unit; split: sharing it
+// with the unit's other workgroups) and at least all its work at the whole
+// GPU's rate; the split is taken when the time it saves by that estimate
+// beats the merge's cost by kSplitMargin.
+template <int D, bool LONG>
+KeySplit plan_split_for(int B, int H, int S, bool causal, int n_cu) {
+  using SH = Shape<D, LONG>;
+  KeySplit ks{};
+  const long long Br = SH::kBr, Bc = SH::kBc, rho = Br / Bc;
+  const long long slots = (long long)n_cu * Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long n_qt = (S + Br - 1) / Br, n_bh = (long long)B * H, n_t = (S + Bc - 1) / Bc;
+  const long long n_wg = n_qt * n_bh;
+  const bool one_per_cu = Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves < 2;
+  const long long max_wg = !causal ? n_cu / 2 : one_per_cu ? slots : slots / 2;
+  if (slots < 1 || n_qt < 2 || n_wg > max_wg) return ks;
+  long long ct, m = 0, n_split, row0;
+  // merged rows x chunks (the partials), merged rows, and all key tiles
+  double part_rows, merged_rows, all_tiles;
+  if (causal) {
+    const long long tiles = n_bh * (rho * (n_qt - 1) * n_qt / 2 + n_t);
+    all_tiles = (double)tiles;
+    const long long per_slot = (tiles + slots - 1) / slots;
+    m = (per_slot + rho / 2) / rho;
+    const long long m_min = (kSplitMinChunkKeys + Br - 1) / Br;
+    if (m < m_min) m = m_min;
+    if (m >= n_qt) return ks;
+    ct = m * rho;
+    n_split = (n_qt - 1) / m + 1;
+    row0 = m * Br;
+    double pr = 0;
+    for (long long t = m; t < n_qt; ++t) pr += (double)(t / m + 1) * (double)Br;
+    part_rows = pr * (double)n_bh;
+    merged_rows = (double)(S - row0) * (double)n_bh;
+  } else {
+    const long long per_tile = n_cu / n_wg;  // chunks per query tile, one per compute unit
+    ct = (n_t + per_tile - 1) / per_tile;
+    const long long ct_min = (kSplitMinChunkKeys + Bc - 1) / Bc;
+    if (ct < ct_min) ct = ct_min;
+    n_split = (n_t + ct - 1) / ct;
+    if (n_split < 2) return ks;
+    row0 = 0;
+    merged_rows = (double)S * (double)n_bh;
+    part_rows = merged_rows * (double)n_split;
+    all_tiles = (double)n_wg * (double)n_t;
+  }
+  const int di = D == 64 ? 0 : D == 128 ? 1 : 2;
+  const long long per_cu = slots / n_cu > 0 ? slots / n_cu : 1;  // workgroups a unit holds
+  const double tile_flops = 4.0 * (double)Br * (double)Bc * D;
+  const double gpu_sec = all_tiles * tile_flops / ((double)n_cu * kCuFlopsFull[di]);
+  // a causal chunk shares its unit with the unit's other workgroups; a
+  // non-causal one has it alone
+  const double chunk_sec = causal ? (double)ct * tile_flops * (double)per_cu / kCuFlopsFull[di]
+                                  : (double)ct * tile_flops / kCuFlopsAlone[di];
+  const double saved =
+      std::max((double)n_t * tile_flops / kCuFlopsAlone[di], gpu_sec) - std::max(chunk_sec, gpu_sec);
+  const double part_bytes = part_rows * (D * 4.0 + 12.0);
+  const double merge = kMergeFixedSec + (part_bytes + merged_rows * D * 2.0) / kMergeBytesPerSec +
+                       part_bytes / kPartialWriteBytesPerSec;
+  if (saved < kSplitMargin * merge) return ks;
+  ks.m = (int)m;
+  ks.ct = (int)ct;
+  ks.n_split = (int)n_split;
+  ks.row0 = (int)row0;
+  ks.n_qt = (int)n_qt;
+  return ks;
+}
+
+KeySplit plan_split(int D, int B, int H, int S, bool causal, int n_cu) {
+  switch (D) {
+    case 64:
+      return S >= FA2_D64_LONG_S ? plan_split_for<64, true>(B, H, S, causal, n_cu)
+                                 : plan_split_for<64, false>(B, H, S, causal, n_cu);
+    case 128: return plan_split_for<128, false>(B, H, S, causal, n_cu);
+    default: return plan_split_for<256, false>(B, H, S, causal, n_cu);
+  }
+}
+
+// Workspace bytes of a key split (0 for none).
+size_t split_workspace_bytes(const KeySplit& ks, int B, int H, int S, int D) {
+  return ks.ct == 0 ? 0 : chunk_workspace_bytes(B, H, S - ks.row0, D, ks.n_split);
 }
 
 hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k, const void* v,
                       void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
-                      int n_cu, hipStream_t stream) {
+                      const KeySplit& ks, int n_cu, hipStream_t stream) {
   switch (D) {
     case 64:
       return S >= FA2_D64_LONG_S
-                 ? launch_dtype<64, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
-                                          stream)
-                 : launch_dtype<64, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st,
+                 ? launch_dtype<64, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                          n_cu, stream)
+                 : launch_dtype<64, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
                                            n_cu, stream);
     case 128:
-      return launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
-                                      stream);
+      return launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                      n_cu, stream);
     default:
-      return launch_dtype<256, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, n_cu,
-                                      stream);
+      return launch_dtype<256, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                      n_cu, stream);
   }
 }
 
@@ -621,69 +836,46 @@ extern "C" int fa2_rows_per_workgroup(int D) {
   }
 }
 
-extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                       int H, int S, int D, int causal, float scale, int dtype, void* stream) {
+namespace {
+
+// Checks shared by the prefill entry points, in their documented order,
+// then the launch. strides: nullptr for contiguous tensors, else 12 element
+// strides. balanced: split the keys of long query tiles when the grid is
+// small (fa2_fwd_balanced), with `workspace` for the partials.
+int prefill_call(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int S, int D, const long long* strides, int causal, float scale, int dtype,
+                 bool balanced, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535) return FA2_ERR_SHAPE;
-  if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
-  if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
-  // One head, plus one tile of keys past its end, is addressed with 32-bit
-  // byte offsets (buffer loads): keep it under 2 GiB.
-  if (((long long)S + 256) * D * 2 > (long long)INT32_MAX) return FA2_ERR_SHAPE;
-  const unsigned long long elems =
-      (unsigned long long)B * (unsigned long long)H * (unsigned long long)S * (unsigned long long)D;
-  // the kernel linearises its block index in a 32-bit int
-  const int rows = fa2_rows_per_workgroup(D);
-  const unsigned long long blocks = (((unsigned long long)S + rows - 1) / rows) *
-                                    (unsigned long long)H * (unsigned long long)B;
-  if (blocks > (unsigned long long)INT32_MAX) return FA2_ERR_SHAPE;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
-  if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
-  const size_t tensor_bytes = (size_t)elems * 2;
-  const size_t lse_bytes = (size_t)B * H * S * sizeof(float);
-  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
-      overlaps(o, tensor_bytes, v, tensor_bytes) || overlaps(lse, lse_bytes, q, tensor_bytes) ||
-      overlaps(lse, lse_bytes, k, tensor_bytes) || overlaps(lse, lse_bytes, v, tensor_bytes) ||
-      overlaps(lse, lse_bytes, o, tensor_bytes))
-    return FA2_ERR_ALIAS;
-  int n_cu = 0;
-  const int dev = check_device(&n_cu);
-  if (dev != FA2_OK) return dev;
-
-  (void)hipGetLastError();  // start from a clean error state
-  const hipError_t err = launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale, nullptr,
-                                    n_cu, (hipStream_t)stream);
-  return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
-}
-
-extern "C" int fa2_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int S, int D, const long long* strides, int causal,
-                               float scale, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse || !strides) return FA2_ERR_NULL;
   if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535) return FA2_ERR_SHAPE;
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
   if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
   // every stride in [0, 2^40], a multiple of 8 elements (16-byte rows), and
   // each sequence stride at least D
-  for (int i = 0; i < 12; ++i) {
-    const long long x = strides[i];
-    if (x < 0 || x > (1LL << 40) || (x & 7)) return FA2_ERR_STRIDE;
-    if (i % 3 == 2 && x < D) return FA2_ERR_STRIDE;
+  Strides st{(long long)H * S * D, (long long)S * D, D, (long long)H * S * D,
+             (long long)S * D,     D,                 (long long)H * S * D, (long long)S * D,
+             D,                    (long long)H * S * D, (long long)S * D, D};
+  if (strides) {
+    for (int i = 0; i < 12; ++i) {
+      const long long x = strides[i];
+      if (x < 0 || x > (1LL << 40) || (x & 7)) return FA2_ERR_STRIDE;
+      if (i % 3 == 2 && x < D) return FA2_ERR_STRIDE;
+    }
+    st = Strides{strides[0], strides[1], strides[2],  strides[3], strides[4],  strides[5],
+                 strides[6], strides[7], strides[8],  strides[9], strides[10], strides[11]};
   }
-  const Strides st{strides[0], strides[1], strides[2],  strides[3], strides[4],  strides[5],
-                   strides[6], strides[7], strides[8],  strides[9], strides[10], strides[11]};
   // one head of K or V, plus a tile of rows past its end, within 32-bit byte
   // offsets (buffer loads)
   if (((long long)S + 256) * st.ks * 2 > (long long)INT32_MAX ||
       ((long long)S + 256) * st.vs * 2 > (long long)INT32_MAX)
     return FA2_ERR_SHAPE;
+  // the kernel linearises its block index in a 32-bit int (a key split
+  // only runs on grids of a few thousand workgroups)
   const int rows = fa2_rows_per_workgroup(D);
   const unsigned long long blocks = (((unsigned long long)S + rows - 1) / rows) *
                                     (unsigned long long)H * (unsigned long long)B;
   if (blocks > (unsigned long long)INT32_MAX) return FA2_ERR_SHAPE;
   // the output's rows must not share memory
-  if (!rows_disjoint(B, H, S, D, st.ob, st.oh, st.os)) return FA2_ERR_STRIDE;
+  if (strides && !rows_disjoint(B, H, S, D, st.ob, st.oh, st.os)) return FA2_ERR_STRIDE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
   if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
@@ -701,8 +893,56 @@ extern "C" int fa2_fwd_strided(const void* q, const void* k, const void* v, void
   const int dev = check_device(&n_cu);
   if (dev != FA2_OK) return dev;
 
-  (void)hipGetLastError();
-  const hipError_t err = launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale, &st, n_cu,
-                                    (hipStream_t)stream);
+  KeySplit ks{};
+  if (balanced) {
+    ks = plan_split(D, B, H, S, causal != 0, n_cu);
+    const size_t need = split_workspace_bytes(ks, B, H, S, D);
+    if (need > 0) {
+      if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need)
+        return FA2_ERR_WORKSPACE;
+      if (overlaps(workspace, need, q, qe) || overlaps(workspace, need, k, ke) ||
+          overlaps(workspace, need, v, ve) || overlaps(workspace, need, o, oe) ||
+          overlaps(workspace, need, lse, lse_bytes))
+        return FA2_ERR_ALIAS;
+      ks.part_o = (float*)workspace;
+      ks.part_ml =
+          (float*)((char*)workspace + chunk_part_o_bytes(B, H, S - ks.row0, D, ks.n_split));
+    }
+  }
+
+  (void)hipGetLastError();  // start from a clean error state
+  const hipError_t err = launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale,
+                                    strides ? &st : nullptr, ks, n_cu, (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int S, int D, int causal, float scale, int dtype, void* stream) {
+  return prefill_call(q, k, v, o, lse, B, H, S, D, nullptr, causal, scale, dtype, false, nullptr,
+                      0, stream);
+}
+
+extern "C" int fa2_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int S, int D, const long long* strides, int causal,
+                               float scale, int dtype, void* stream) {
+  if (!strides) return FA2_ERR_NULL;
+  return prefill_call(q, k, v, o, lse, B, H, S, D, strides, causal, scale, dtype, false, nullptr,
+                      0, stream);
+}
+
+extern "C" size_t fa2_fwd_balanced_workspace_bytes(int B, int H, int S, int D, int causal) {
+  if (B < 1 || H < 1 || S < 1 || !(D == 64 || D == 128 || D == 256)) return 0;
+  int n_cu = 0;
+  if (check_device(&n_cu) != FA2_OK) return 0;
+  return split_workspace_bytes(plan_split(D, B, H, S, causal != 0, n_cu), B, H, S, D);
+}
+
+extern "C" int fa2_fwd_balanced(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int S, int D, const long long* strides, int causal,
+                                float scale, int dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return prefill_call(q, k, v, o, lse, B, H, S, D, strides, causal, scale, dtype, true, workspace,
+                      workspace_bytes, stream);
 }

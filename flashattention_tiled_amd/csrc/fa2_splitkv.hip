@@ -11,11 +11,7 @@
 // its keys and a second kernel merges them. That is the split-then-combine
 // structure of jared-hpc Lecture 6 ("FA2 change 2": parts of the KV range
 // computed apart and their (m, l) combined at the end), moved from warps to
-// workgroups. The merge is the guide's rescaling algebra applied across
-// chunks: with M = max_g m_g and w_g = 2^(m_g - M),
-//   O = sum_g w_g O~_g / sum_g w_g l'_g,   lse = ln2 (M + log2 sum_g w_g l_g),
-// l_g summing P as computed and l'_g summing P as rounded for the P V
-// product (the two sums of the prefill kernel).
+// workgroups; fa2_combine.h holds the merge.
 //
 // The partial kernel runs one wave per workgroup: a 32-row query block (rows
 // past Sq are zero and never stored) against one key chunk, streamed through
@@ -25,13 +21,13 @@
 // running row max per tile (no lazy reference point), which also covers rows
 // that have no key in a chunk (their partial is m = -inf, l = 0).
 //
-// Workspace (caller-owned device memory, fp32):
-//   part_o  [B*H][n_split][Sq][D]   unnormalised O~ of each chunk
-//   part_ml [B*H][n_split][Sq][3]   m (base 2), l (P as computed), l (P as rounded)
-// part_ml starts at the part_o size rounded up to 256 bytes.
+// Workspace (caller-owned device memory, fp32): the chunk partials of
+// fa2_combine.h for all Sq rows (row0 = 0); part_ml starts at the part_o
+// size rounded up to 256 bytes.
 
 #include "fa2_tile.h"
 #include "fa2_host.h"
+#include "fa2_combine.h"
 
 using fa2_host::check_device;
 using fa2_host::extent_bytes;
@@ -50,13 +46,6 @@ template <int D, bool KV8 = false> struct SplitTile {
   static_assert(kTileBytes % 1024 == 0, "a tile is whole 1 KiB wave loads");
 };
 
-size_t splitkv_part_o_bytes(int B, int H, int Sq, int D, int n_split) {
-  const size_t b = (size_t)B * H * n_split * Sq * D * sizeof(float);
-  return (b + 255) / 256 * 256;
-}
-size_t splitkv_workspace_bytes(int B, int H, int Sq, int D, int n_split) {
-  return splitkv_part_o_bytes(B, H, Sq, D, n_split) + (size_t)B * H * n_split * Sq * 3 * sizeof(float);
-}
 
 // ---- FP8 (e4m3) K and V ------------------------------------------------
 // Codes (OCP FP8 e4m3: sign, 4 exponent bits of bias 7, 3 mantissa bits)
@@ -385,87 +374,6 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   }
 }
 
-// Merge the chunks of each query row: one wave per row, D / 64 columns per
-// lane. The chunks' (m, l, l') are read 64 at a time, one chunk per lane,
-// and reduced across the wave; the weighted O~ rows are then summed four
-// chunks at a time, so that their loads overlap.
-template <int D, int DT>
-__global__ __launch_bounds__(256) void fa2_splitkv_combine_kernel(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int n_rows, int H, int Sq, int n_split, long long ob, long long oh,
-    long long os) {
-  using E = Elem<DT>;
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= n_rows) return;  // whole waves leave together
-  const int bh = r / Sq, i = r % Sq;
-  const size_t first = (size_t)bh * n_split * Sq + i;  // partial row of chunk 0
-  // M = max of m over the chunks that saw a key
-  float mx = -INFINITY;
-  for (int g = lane; g < n_split; g += 64) {
-    const float* ml = part_ml + (first + (size_t)g * Sq) * 3;
-    if (ml[2] > 0.f) mx = fmaxf(mx, ml[0]);
-  }
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  float den = 0.f, lsum = 0.f;
-  for (int g0 = 0; g0 < n_split; g0 += 64) {
-    // this lane's chunk of the block: w = 2^(m - M), and its share of the sums
-    float w = 0.f;
-    if (g0 + lane < n_split) {
-      const float* ml = part_ml + (first + (size_t)(g0 + lane) * Sq) * 3;
-      if (ml[2] > 0.f) {
-        w = __builtin_amdgcn_exp2f(ml[0] - mx);
-        lsum += w * ml[1];
-        den += w * ml[2];
-      }
-    }
-    const int nb = min(64, n_split - g0);
-    int j = 0;
-    for (; j + 4 <= nb; j += 4) {
-      float wj[4], val[4][PER];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wj[u] = __shfl(w, j + u);
-        const float* po = part_o + (first + (size_t)(g0 + j + u) * Sq) * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) val[u][e] = po[e];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) num[e] += wj[u] * val[u][e];
-    }
-    for (; j < nb; ++j) {
-      const float wj = __shfl(w, j);
-      const float* po = part_o + (first + (size_t)(g0 + j) * Sq) * D + lane * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += wj * po[e];
-    }
-  }
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) {
-    lsum += __shfl_xor(lsum, s);
-    den += __shfl_xor(den, s);
-  }
-  const float inv = 1.0f / den;
-  uint16_t* orow = o + (size_t)((bh / H) * ob + (bh % H) * oh + (long long)i * os);
-#pragma unroll
-  for (int e = 0; e < PER; e += 2) {
-    const uint32_t pk = E::pack2(num[e] * inv, (e + 1 < PER ? num[e + 1] : 0.f) * inv);
-    if (PER >= 2) {
-      *(uint32_t*)(orow + lane * PER + e) = pk;
-    } else {
-      orow[lane] = (uint16_t)(pk & 0xffffu);
-    }
-  }
-  if (lane == 0) lse[r] = (mx + __builtin_amdgcn_logf(lsum)) * kLn2;
-}
-
 // Key chunks per (b, h) for a launch: enough workgroups for about two on
 // every compute unit with 16-bit K and V, four with FP8 (a chunk then holds
 // half the bytes, and the code conversions want more waves beside the
@@ -496,17 +404,15 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, 
   const int n_eff = (n_tiles + chunk_tiles - 1) / chunk_tiles;
   const int n_qblk = (Sq + 31) / 32;
   float* part_o = (float*)ws;
-  float* part_ml = (float*)((char*)ws + splitkv_part_o_bytes(B, H, Sq, D, n_eff));
+  float* part_ml = (float*)((char*)ws + chunk_part_o_bytes(B, H, Sq, D, n_eff));
   const dim3 grid((unsigned)(n_eff * n_qblk), (unsigned)H, (unsigned)B);
   fa2_splitkv_partial_kernel<D, DT, CAUSAL, KV8><<<grid, dim3(64), 0, stream>>>(
       (const uint16_t*)q, k, v, part_o, part_ml, Sq, Sk, n_eff, chunk_tiles * ST::kBc,
       scale * kLog2e * k_mult, v_mult, st);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int n_rows = B * H * Sq;
-  fa2_splitkv_combine_kernel<D, DT><<<dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
-      part_o, part_ml, (uint16_t*)o, lse, n_rows, H, Sq, n_eff, st.ob, st.oh, st.os);
-  return hipGetLastError();
+  return launch_combine<D, DT>(part_o, part_ml, o, lse, B * H, H, Sq, 0, 0, n_eff, st.ob, st.oh,
+                               st.os, stream);
 }
 
 template <int D, int DT, bool KV8>
@@ -603,7 +509,7 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
     n_split = splitkv_default_splits(B, H, Sq, Sk, n_cu, kv_elem_bytes == 1);
   }
   if (n_split > 65536) return FA2_ERR_SHAPE;
-  const size_t need = splitkv_workspace_bytes(B, H, Sq, D, n_split);
+  const size_t need = chunk_workspace_bytes(B, H, Sq, D, n_split);
   if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return FA2_ERR_WORKSPACE;
   // overlap, by the byte range each tensor spans
   const size_t q_bytes = extent_bytes(B, H, Sq, D, st.qb, st.qh, st.qs, 2);
@@ -659,7 +565,7 @@ extern "C" size_t fa2_splitkv_workspace_bytes(int B, int H, int Sq, int Sk, int 
   // n_split = 0: enough for the default of either entry point (the FP8
   // default is never below the 16-bit one)
   if (n_split == 0) n_split = default_splits_here(B, H, Sq, Sk, true);
-  return splitkv_workspace_bytes(B, H, Sq, D, n_split);
+  return chunk_workspace_bytes(B, H, Sq, D, n_split);
 }
 
 extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,

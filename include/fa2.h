@@ -119,6 +119,49 @@ int fa2_fwd_strided(const void *q, const void *k, const void *v, void *o, float 
                     int B, int H, int S, int D, const long long *strides, int causal,
                     float scale, int dtype, void *stream);
 
+/*
+ * fa2_fwd_balanced -- fa2_fwd (strides NULL) or fa2_fwd_strided (strides
+ * given), with the keys of long query tiles split across workgroups when
+ * the grid is too small to keep the GPU busy to its end.
+ *
+ * The sequence-parallel grid of FlashAttention-2 (jared-hpc Lecture 6, "FA2
+ * change 1") has ceil(S / rows) * H * B workgroups. When that is under two
+ * rounds of the workgroups the GPU holds at once, the launch ends on its
+ * longest tile -- under causal masking, the last query tile of a head, with
+ * all S keys against the average tile's S / 2 -- and part of the GPU idles
+ * meanwhile. This call then cuts each query tile's keys into chunks that
+ * run as separate workgroups, longest first, and merges the chunks' partial
+ * (O~, m, l) with the rescaling algebra of the infra.bea.ai FlashAttention
+ * V2 guide ("Optimization 2: Delay Rescaling") in a second kernel on the
+ * same stream -- "FA2 change 2" of the lecture (parts of the KV range
+ * computed apart, their (m, l) combined at the end) across workgroups.
+ * Larger grids, and shapes where the split would not pay, run exactly the
+ * fa2_fwd / fa2_fwd_strided launch.
+ *
+ * workspace        device memory for the partials, at least
+ *                  fa2_fwd_balanced_workspace_bytes(B, H, S, D, causal)
+ *                  bytes, 16-byte aligned, not overlapping any tensor;
+ *                  caller-owned, contents on entry ignored. May be NULL when
+ *                  that size is 0.
+ * workspace_bytes  its size in bytes.
+ * Other arguments, the arithmetic and the ownership rules are those of
+ * fa2_fwd_strided (strides given) or fa2_fwd (NULL). Results agree with
+ * those calls to within rounding: a split row's O is the merge of its
+ * chunks' fp32 partials, rounded once. Returns FA2_ERR_WORKSPACE for a
+ * missing, misaligned or short workspace (checked after the device, as the
+ * split depends on the device's compute units), FA2_ERR_ALIAS for one that
+ * overlaps a tensor, otherwise the codes of fa2_fwd / fa2_fwd_strided.
+ */
+int fa2_fwd_balanced(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int H, int S, int D, const long long *strides, int causal,
+                     float scale, int dtype, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+/* Workspace bytes fa2_fwd_balanced needs for this shape on the current
+ * device: 0 when it runs unsplit, when the arguments are out of range, or
+ * when there is no usable device. */
+size_t fa2_fwd_balanced_workspace_bytes(int B, int H, int S, int D, int causal);
+
 /* 1 when fa2_fwd has a kernel for head dimension D and dtype, else 0. */
 int fa2_supported(int D, int dtype);
 

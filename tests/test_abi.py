@@ -129,7 +129,7 @@ def _call(**kw):
     return fa.fa2_fwd(**args)
 
 
-@pytest.mark.parametrize("kw,status", [
+_FWD_CASES = [
     (dict(q=None), fa.FA2_ERR_NULL),
     (dict(k=0), fa.FA2_ERR_NULL),
     (dict(v=None), fa.FA2_ERR_NULL),
@@ -157,7 +157,10 @@ def _call(**kw):
     (dict(o=K + 16), fa.FA2_ERR_ALIAS),
     (dict(lse=V + _N - 4), fa.FA2_ERR_ALIAS),
     (dict(lse=O + 64), fa.FA2_ERR_ALIAS),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", _FWD_CASES)
 def test_validation_status(lib, kw, status):
     assert _call(**kw) == status
 
@@ -210,7 +213,7 @@ def _with(base, **idx):
     return out
 
 
-@pytest.mark.parametrize("kw,status", [
+_STRIDED_CASES = [
     (dict(q=None), fa.FA2_ERR_NULL),
     (dict(strides=None), fa.FA2_ERR_NULL),
     (dict(S=0), fa.FA2_ERR_SHAPE),
@@ -229,7 +232,10 @@ def _with(base, **idx):
     (dict(scale=float("inf")), fa.FA2_ERR_SCALE),
     (dict(o=SQ + 1024), fa.FA2_ERR_ALIAS),
     (dict(lse=SV + 4096), fa.FA2_ERR_ALIAS),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", _STRIDED_CASES)
 def test_strided_validation_status(lib, kw, status):
     assert _call_strided(**kw) == status
 
@@ -246,6 +252,56 @@ def test_strided_valid_layouts_reach_the_device_check(lib, strides):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; the fake pointers must not be launched on")
     assert _call_strided(strides=strides) == fa.FA2_ERR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# balanced (key-split) entry point: fa2_fwd's checks with strides NULL,
+# fa2_fwd_strided's with strides, in the same order; the workspace is
+# checked after the device (the split depends on its compute units)
+# ---------------------------------------------------------------------------
+def _call_balanced(strided, **kw):
+    if strided:
+        args = dict(q=SQ, k=SK, v=SV, o=SO, lse=SL, B=_B, H=_H, S=_S, D=64,
+                    strides=list(_CONTIG))
+    else:
+        args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, S=64, D=64, strides=None)
+    args.update(causal=0, scale=0.125, dtype=fa.FA2_F16, workspace=None, workspace_bytes=0,
+                stream=None)
+    args.update(kw)
+    return fa.fa2_fwd_balanced(**args)
+
+
+@pytest.mark.parametrize("kw,status", _FWD_CASES)
+def test_balanced_validation_status(lib, kw, status):
+    assert _call_balanced(False, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [c for c in _STRIDED_CASES if "strides" not in c[0]
+                                       or c[0]["strides"] is not None])
+def test_balanced_strided_validation_status(lib, kw, status):
+    assert _call_balanced(True, **kw) == status
+
+
+def test_balanced_valid_calls_reach_the_device_check(lib):
+    """Valid calls, with or without strides and with no workspace, pass every
+    check before the device lookup (no GPU here: FA2_ERR_NO_DEVICE)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call_balanced(False) == fa.FA2_ERR_NO_DEVICE
+    assert _call_balanced(True) == fa.FA2_ERR_NO_DEVICE
+    assert _call_balanced(True, strides=list(_BSHD), causal=1) == fa.FA2_ERR_NO_DEVICE
+
+
+def test_balanced_workspace_bytes_without_a_device(lib):
+    """The split depends on the device's compute units: with no device, or
+    with arguments out of range, the size is 0."""
+    import torch
+    assert fa.fa2_fwd_balanced_workspace_bytes(1, 4, 8192, 96, 1) == 0
+    assert fa.fa2_fwd_balanced_workspace_bytes(0, 4, 8192, 128, 1) == 0
+    assert fa.fa2_fwd_balanced_workspace_bytes(1, 4, -1, 128, 1) == 0
+    if torch.cuda.device_count() == 0:
+        assert fa.fa2_fwd_balanced_workspace_bytes(1, 4, 8192, 128, 1) == 0
 
 
 # ---------------------------------------------------------------------------

@@ -12,8 +12,9 @@ import numpy as np
 import pytest
 import torch
 
+import flashattention_tiled_amd as fa
 import workloads as wl
-from gpu_helpers import (announce, assert_parity, oracle_full, oracle_rows, run_gpu,
+from gpu_helpers import (DEV, announce, assert_parity, oracle_full, oracle_rows, run_gpu,
                          sample_rows)
 
 pytestmark = pytest.mark.gpu
@@ -139,6 +140,14 @@ def test_full_size_sampled(w):
     o_s = o.reshape(-1, w.D)[torch.from_numpy(rows)]
     lse_s = lse.reshape(-1)[torch.from_numpy(rows)]
     assert_parity(o_s, lse_s, o_ref, lse_ref, w.dtype, f"{w.name} ({len(rows)} rows)")
+    if fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, int(w.causal)) > 0:
+        # attention() split this shape's keys: check the unsplit launch too
+        qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+        o1, lse1 = fa.attention(qd, kd, vd, causal=w.causal, scale=w.scale, balanced=False)
+        torch.cuda.synchronize()
+        o_s = o1.cpu().reshape(-1, w.D)[torch.from_numpy(rows)]
+        lse_s = lse1.cpu().reshape(-1)[torch.from_numpy(rows)]
+        assert_parity(o_s, lse_s, o_ref, lse_ref, w.dtype, f"{w.name} unsplit ({len(rows)} rows)")
 
 
 @pytest.mark.parametrize("S", [8192, 8223, 12001])
