@@ -59,16 +59,22 @@ constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile
 //   kWavesPerSimd  waves per SIMD the register budget is sized for
 //   kLoadEvery     phase-1 k-steps between this wave's tile-load blocks (0: all
 //                  at the start of the step)
-// K and V each have a two-stage LDS ring: iteration j reads K of tile j + 1
-// and V of tile j while K of tile j + 2 and V of tile j + 1 load.
-// The defaults are the best of a sweep over these five values on the
-// benchmark shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides
-// one, as "waves, row blocks, keys, waves per SIMD, load spacing". D = 64 has
+//   kStages        stages of the K ring and of the V ring (default 2)
+// Iteration j reads K of tile j + 1 and V of tile j while K of tile
+// j + kStages and V of tile j + kStages - 1 load, so a tile's loads have
+// kStages - 1 iterations to land. Two stages fit two workgroups per compute
+// unit at D <= 128; D = 256 holds one workgroup per unit (its registers allow
+// one wave per SIMD), whose single wave per SIMD cannot hide a load behind
+// another workgroup's work, and it spends the spare LDS on a deeper ring.
+// The defaults are the best of a sweep over these values on the benchmark
+// shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides one, as
+// "waves, row blocks, keys, waves per SIMD, load spacing[, stages]". D = 64 has
 // a second configuration for sequences of at least FA2_D64_LONG_S (the LONG
 // tile): 32-key tiles at four waves per SIMD, 2-4% faster there and up to
 // 20% slower on short sequences.
-template <int W, int RB, int BC, int WPS, int LE> struct TileCfg {
-  static constexpr int kWaves = W, kRowBlocks = RB, kBc = BC, kWavesPerSimd = WPS, kLoadEvery = LE;
+template <int W, int RB, int BC, int WPS, int LE, int NST = 2> struct TileCfg {
+  static constexpr int kWaves = W, kRowBlocks = RB, kBc = BC, kWavesPerSimd = WPS, kLoadEvery = LE,
+                       kStages = NST;
 };
 #ifndef FA2_TILE_D64
 #define FA2_TILE_D64 4, 1, 64, 2, 1
@@ -83,7 +89,7 @@ template <int W, int RB, int BC, int WPS, int LE> struct TileCfg {
 #define FA2_TILE_D128 4, 1, 64, 2, 2
 #endif
 #ifndef FA2_TILE_D256
-#define FA2_TILE_D256 4, 1, 32, 1, 0
+#define FA2_TILE_D256 4, 1, 32, 1, 1, 4
 #endif
 template <int D, bool LONG = false> struct Tile;
 template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};
@@ -101,8 +107,10 @@ template <int D, bool LONG = false> struct Shape {
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per key row
   static constexpr int kTileBytes = kBc * D * 2;     // one K or one V tile
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per K (or V) tile
-  static constexpr int kLdsBytes = 4 * kTileBytes;   // K ring (2) + V ring (2)
+  static constexpr int kStages = Tile<D, LONG>::kStages;
+  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;  // K ring + V ring
   static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+  static_assert(kStages >= 2 && (kStages - 2) * 2 * kLoadsPerWave < 64, "ring depth");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
@@ -387,9 +395,11 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   constexpr int NDS = D / 16;   // k-steps of 16 over the head dim (S^T product)
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O^T
 
-  // K ring (stages 0, 1) then V ring (stages 0, 1), TB bytes each.
+  constexpr int NST = SH::kStages;
+
+  // K ring (stages 0 .. NST - 1) then V ring (stages 0 .. NST - 1), TB bytes each.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SH::kLdsBytes];
-  constexpr uint32_t kK0 = 0, kK1 = TB, kV0 = 2 * TB, kV1 = 3 * TB;
+  constexpr uint32_t kK0 = 0, kK1 = TB, kV0 = NST * TB, kV1 = (NST + 1) * TB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -527,16 +537,32 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   // Software pipeline. Iteration j computes the scores of tile j + 1 on the
   // matrix cores while the vector unit turns tile j's scores into P, then the
   // P V product of tile j.
-  // At its top every load issued in iteration j - 1 (K of tile j + 1, V of
-  // tile j) has landed, and after the barrier every wave is done with
-  // iteration j - 1, so K of tile j + 2 goes into tile j's K stage and V of
-  // tile j + 1 into tile j - 1's V stage.
+  // At its top every load issued in iteration j - NST + 1 (K of tile j + 1,
+  // V of tile j) has landed -- this wave's later loads, 2 LPW per iteration,
+  // may still be in flight -- and after the barrier every wave is done with
+  // iteration j - 1, so K of tile j + NST goes into tile j's K stage and V of
+  // tile j + NST - 1 into tile j - 1's V stage. Tile t sits in stage t % NST
+  // of each ring.
   load_tile_rsrc<LPW>(k_tile(k_bytes, t0), smem + kK0, wave, k_off);
-  load_tile_rsrc<LPW>(v_tile(v_bytes, t0), smem + kV0, wave, v_off);
-  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(k_bytes, t0 + 1), smem + kK1, wave, k_off);
+  if constexpr (NST == 2) {
+    load_tile_rsrc<LPW>(v_tile(v_bytes, t0), smem + kV0, wave, v_off);
+    if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(k_bytes, t0 + 1), smem + kK1, wave, k_off);
+  } else {
+    // the loads iterations 1 - NST .. -1 would have issued, K then V of each
+    // (a tile past the workgroup's last gets a zero-length buffer)
+#pragma unroll
+    for (int i = 1; i < NST; ++i) {
+      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? k_bytes : 0u, t0 + i), smem + kK0 + i * TB, wave,
+                          k_off);
+      load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? v_bytes : 0u, t0 + i - 1),
+                          smem + kV0 + (i - 1) * TB, wave, v_off);
+    }
+  }
 
   f32x16 s_a[RB][NKB], s_b[RB][NKB];
   float ce_a[RB], ce_b[RB];
+  // all of them (and the Q loads, which the compiler may have issued after
+  // them) before the first tile's scores
   wait_vm_lgkm0<0>();
   workgroup_barrier();
   if (n_act > 0) {
@@ -553,17 +579,29 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   auto step = [&](auto par, int j, f32x16 (&cur)[RB][NKB], float (&ce_cur)[RB],
                   f32x16 (&nxt)[RB][NKB], float (&ce_nxt)[RB]) {
     constexpr int PAR = decltype(par)::value;
-    constexpr uint32_t k_next = PAR ? kK0 : kK1;  // K of tile j + 1
-    constexpr uint32_t k_free = PAR ? kK1 : kK0;  // K of tile j (done)
-    constexpr uint32_t v_cur = PAR ? kV1 : kV0;   // V of tile j
-    constexpr uint32_t v_free = PAR ? kV0 : kV1;  // V of tile j - 1 (done)
-    wait_vm_lgkm0<0>();
+    uint32_t k_next, k_free, v_cur, v_free;  // K of tile j + 1, of tile j (done);
+                                             // V of tile j, of tile j - 1 (done)
+    if constexpr (NST == 2) {
+      k_next = PAR ? kK0 : kK1;
+      k_free = PAR ? kK1 : kK0;
+      v_cur = PAR ? kV1 : kV0;
+      v_free = PAR ? kV0 : kV1;
+    } else {
+      const int sj = wave_uniform(j % NST);  // stage of tile j
+      const int sn = sj + 1 == NST ? 0 : sj + 1, sp = sj == 0 ? NST - 1 : sj - 1;
+      k_next = kK0 + (uint32_t)(sn * TB);
+      k_free = kK0 + (uint32_t)(sj * TB);
+      v_cur = kV0 + (uint32_t)(sj * TB);
+      v_free = kV0 + (uint32_t)(sp * TB);
+    }
+    wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
     workgroup_barrier();
-    // K of tile j + 2 and V of tile j + 1; a tile past the workgroup's last
-    // gets a zero-length buffer, so its loads only write zeros to a free stage
+    // K of tile j + NST and V of tile j + NST - 1; a tile past the
+    // workgroup's last gets a zero-length buffer, so its loads only write
+    // zeros to a free stage
     const StepLoads<LPW> ld{
-        k_tile(j + 2 < n_tiles ? k_bytes : 0u, t0 + j + 2),
-        v_tile(j + 1 < n_tiles ? v_bytes : 0u, t0 + j + 1),
+        k_tile(j + NST < n_tiles ? k_bytes : 0u, t0 + j + NST),
+        v_tile(j + NST - 1 < n_tiles ? v_bytes : 0u, t0 + j + NST - 1),
         smem + k_free, smem + v_free, k_off, v_off, wave};
     if (j < n_act) {
       // scores of tile j + 1 || probabilities of tile j, then P V of tile j

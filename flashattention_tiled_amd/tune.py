@@ -2,7 +2,8 @@
 cookbook notebook's exercise "Autotune BLOCK_M, BLOCK_N, num_warps".
 
 Each candidate sets one head dim's tile configuration (waves per workgroup,
-32-row blocks per wave, keys per tile, waves per SIMD, load spacing; so
+32-row blocks per wave, keys per tile, waves per SIMD, load spacing and,
+optionally, the depth of the K and V LDS rings (2 if absent); so
 B_r = 32 * waves * row blocks and B_c = keys per tile) through the
 FA2_TILE_D<D> macro of csrc/fa2_fwd.hip and is built into a library of its
 own (without the library's switch to its long-sequence D = 64 tile, so that
@@ -34,31 +35,38 @@ import time
 
 from .build import CSRC, HIP_FLAGS, HIPCC, INCLUDE, ROOT, SOURCES
 
-# (waves, row blocks, keys per tile, waves per SIMD, load spacing); the first
-# entry of each list is the library default
+# (waves, row blocks, keys per tile, waves per SIMD, load spacing[, stages]);
+# the first entry of each list is the library default
 CANDIDATES = {
     64: [(4, 1, 64, 2, 1), (4, 1, 64, 2, 0), (4, 1, 64, 2, 2), (4, 1, 32, 4, 0),
          (4, 1, 32, 2, 0), (8, 1, 64, 2, 0), (2, 1, 64, 2, 0), (4, 2, 64, 1, 0),
          (4, 1, 128, 1, 0)],
     128: [(4, 1, 64, 2, 2), (4, 1, 64, 2, 0), (4, 1, 64, 2, 1), (4, 1, 64, 2, 4),
           (8, 1, 64, 2, 2), (4, 1, 32, 2, 0), (2, 1, 64, 2, 1), (4, 1, 128, 1, 2)],
-    256: [(4, 1, 32, 1, 0), (4, 1, 32, 1, 1), (8, 1, 32, 1, 0), (2, 1, 32, 1, 0)],
+    256: [(4, 1, 32, 1, 1, 4), (4, 1, 32, 1, 0), (4, 1, 32, 1, 1), (4, 1, 32, 1, 0, 4),
+          (4, 1, 32, 1, 2, 4), (4, 1, 32, 1, 1, 3), (4, 1, 32, 1, 1, 5), (8, 1, 32, 1, 0),
+          (2, 1, 32, 1, 0)],
 }
 
 
 def valid(D: int, cfg) -> bool:
     """The kernel's compile-time conditions on a configuration."""
-    w, rb, bc, wps, le = cfg
+    w, rb, bc, wps, le = cfg[:5]
+    stages = cfg[5] if len(cfg) > 5 else 2
     tile_bytes = bc * D * 2
-    if bc % 32 or tile_bytes % (1024 * w) or 4 * tile_bytes > 160 * 1024 or w * 64 > 1024:
+    if (bc % 32 or tile_bytes % (1024 * w) or 2 * stages * tile_bytes > 160 * 1024
+            or w * 64 > 1024 or stages < 2):
         return False
     lpw = tile_bytes // 1024 // w
+    if (stages - 2) * 2 * lpw >= 64:
+        return False
     ns1 = (D // 16) * (bc // 32)  # phase-1 k-steps per tile
     return le == 0 or (ns1 + le - 1) // le >= 2 * lpw
 
 
 def name(D: int, cfg) -> str:
-    return f"d{D}_w{cfg[0]}_rb{cfg[1]}_bc{cfg[2]}_wps{cfg[3]}_le{cfg[4]}"
+    st = f"_st{cfg[5]}" if len(cfg) > 5 else ""
+    return f"d{D}_w{cfg[0]}_rb{cfg[1]}_bc{cfg[2]}_wps{cfg[3]}_le{cfg[4]}{st}"
 
 
 def _build_one(out: str, D: int, cfg) -> tuple:
