@@ -9,6 +9,7 @@ Prints one JSON line on stdout; diagnostics go to stderr.
     python bench.py --table PATH      # every benchmark shape: fa2_fwd, and fa2_fwd_balanced where it splits
     python bench.py --decode-table PATH   # split-KV decode shapes, GB/s
     python bench.py --layer           # attention layer it/s and peak memory
+    python bench.py --mfma-ceiling    # matrix-core rate and clock on random fp16 data
 
 Metric: TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal masking, and the
 fraction of the MI355X dense fp16/bf16 matrix-core peak (256 CUs x 2.4 GHz x
@@ -327,6 +328,62 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
                 seconds=dt, parity_max_abs_o=o_err, parity_lse_rel=lse_err)
 
 
+def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20):
+    """Rate and clock of the matrix-core ceiling probe (libfa2probe.so): fp16
+    32x32x16 products on random N(0, 1) operands and nothing else, two
+    workgroups per compute unit, median of `launches` HIP-event timed
+    launches after `warmup_min_s` of warm-up. None when the probe is not
+    built."""
+    import ctypes
+
+    import torch
+
+    from flashattention_tiled_amd.build import PROBE_LIB_PATH
+
+    if not os.path.exists(PROBE_LIB_PATH):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB_PATH)  # after torch: shares its HIP runtime
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.fa2_probe_mfma_ceiling.argtypes = [vp, i, i, vp, vp, vp]
+    lib.fa2_probe_mfma_ceiling.restype = i
+    lib.fa2_probe_mfma_flops.argtypes = [i, i]
+    lib.fa2_probe_mfma_flops.restype = ctypes.c_double
+    dev = torch.device("cuda:0")
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_wg, iters = 2 * n_cu, 4096
+    g = torch.Generator("cpu").manual_seed(0)
+    ops = torch.randn(384 * 8, generator=g).to(torch.float16).to(dev)
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(n_wg * 4 * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def launch():
+        st = lib.fa2_probe_mfma_ceiling(ops.data_ptr(), n_wg, iters, sink.data_ptr(),
+                                        clocks.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError(f"fa2_probe_mfma_ceiling status {st}")
+
+    t = time.perf_counter()
+    while time.perf_counter() - t < warmup_min_s:
+        launch()
+        torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        launch()
+        b.record()
+    torch.cuda.synchronize(dev)
+    med = sorted(a.elapsed_time(b) for a, b in ev)[launches // 2]
+    tflops = lib.fa2_probe_mfma_flops(n_wg, iters) / (med * 1e-3) / 1e12
+    ck = clocks.view(-1, 2).cpu().double()
+    # s_memtime counts shader-clock cycles, s_memrealtime a constant 100 MHz
+    ghz = float((ck[:, 0] / ck[:, 1]).mean()) * 0.1
+    return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_TFLOPS, 4),
+            "clock_ghz": round(ghz, 3), "workgroups": n_wg, "ms": round(med, 4),
+            "what": "fp16 32x32x16 matrix-core products on random N(0,1) operands only"}
+
+
 def stats_line(w, r):
     durs = r["durs_ms"]
     avg = sum(durs) / len(durs)
@@ -375,6 +432,10 @@ def main():
                     help="time the attention layer against a score-materialising layer")
     ap.add_argument("--decode-table", default=None,
                     help="time the split-KV path on every decode shape into a CSV")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the matrix-core ceiling probe and print its rate and clock")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="leave the matrix-core ceiling probe out of the bench line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (`steps` times), to "
                          "calibrate the HBM byte counters against a known traffic")
@@ -404,6 +465,9 @@ def main():
     if args.table:
         run_table(args.table, args.steps, args.warmup)
         return
+    if args.mfma_ceiling:
+        print(json.dumps(mfma_ceiling()), flush=True)
+        return
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -431,6 +495,11 @@ def main():
         log(f"[bench] oracle sample: {cpu['sample']}; parity max|dO|={cpu['parity_max_abs_o']:.3e} "
             f"lse_rel={cpu['parity_lse_rel']:.3e}")
 
+    ceiling = None if args.no_ceiling else mfma_ceiling()
+    if ceiling is not None:
+        ceiling["kernel_frac_of_probe"] = round(achieved / ceiling["tflops"], 4)
+        log(f"[bench] matrix-core ceiling probe: {ceiling}")
+
     out = {
         "metric": "attention fwd TFLOP/s and % of fp16 MFMA peak, B=2 H=16 S=8192 D=128 causal",
         "value": round(value, 2),
@@ -451,7 +520,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5)},
+                     "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5),
+                     "mfma_ceiling_probe": ceiling},
         "cpu_baseline": None if cpu is None else {
             k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "parity_sample": None if cpu is None else {

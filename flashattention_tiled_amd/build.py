@@ -42,6 +42,21 @@ def build_library(force: bool = True, extra_flags=None) -> str:
     return LIB_PATH
 
 
+PROBE_SOURCE = os.path.join(CSRC, "fa2_probe.hip")
+PROBE_LIB_PATH = os.path.join(PKG, "libfa2probe.so")
+
+
+def build_probe(force: bool = True) -> str:
+    """Compile the matrix-core ceiling probe (csrc/fa2_probe.hip), a
+    measurement aid kept out of the attention library, into libfa2probe.so."""
+    if force or not os.path.exists(PROBE_LIB_PATH):
+        tmp = PROBE_LIB_PATH + ".tmp"
+        cmd = [HIPCC, *HIP_FLAGS, "-I", INCLUDE, "-o", tmp, PROBE_SOURCE]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, PROBE_LIB_PATH)
+    return PROBE_LIB_PATH
+
+
 def prefill_kernel_sha() -> str:
     """SHA-256 over the prefill kernel's source files (name and bytes of each),
     which keys measurements taken of that kernel to the code they measured."""
@@ -55,3 +70,4 @@ def prefill_kernel_sha() -> str:
 
 if __name__ == "__main__":
     print(build_library())
+    print(build_probe())

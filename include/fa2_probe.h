@@ -1,0 +1,43 @@
+// Measurement aid beside the attention library (libfa2probe.so, a library of
+// its own): a kernel that does nothing but fp16 matrix-core products on
+// random operands, timed by the caller, to give the rate the matrix cores of
+// the GPU actually sustain on data like attention's. The nominal dense
+// fp16/bf16 peak of MI355X (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU) assumes
+// the top clock; under matrix-core load on random data the part lowers its
+// clock to stay within its power limit, and this kernel reports both the
+// rate and the clock it ran at. Not part of the attention path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+// Number of 8 x fp16 operand vectors the kernel reads (6 per lane of a wave:
+// 4 A and 2 B operands, rotated so that consecutive products see different
+// inputs).
+#define FA2_PROBE_OPERAND_VECTORS 384
+
+// FLOPs one launch performs: n_wg workgroups of 4 waves, each wave `iters`
+// rounds of 16 products of v_mfma_f32_32x32x16_f16 (32 x 32 x 16 x 2 FLOPs).
+double fa2_probe_mfma_flops(int n_wg, int iters);
+
+// Enqueue one launch on `stream` (asynchronous, never synchronises).
+//   operands  device, FA2_PROBE_OPERAND_VECTORS x 8 fp16 values (16-byte
+//             aligned), read only; random N(0, 1) values model attention's
+//   n_wg      workgroups (256 threads each; two fit on a compute unit)
+//   iters     rounds per wave, >= 1
+//   sink      device, n_wg x 256 floats: each thread writes one sum of its
+//             results there, so that the products are not optimised away
+//   clocks    device, n_wg x 4 x 2 unsigned 64-bit values: per wave, the
+//             shader-clock ticks (s_memtime) and the constant 100 MHz
+//             reference ticks (s_memrealtime) its loop took
+// Returns 0, or 1 for a null pointer, 2 for n_wg < 1 or iters < 1, 8 when
+// the launch fails. The caller owns every buffer.
+int fa2_probe_mfma_ceiling(const void* operands, int n_wg, int iters, float* sink,
+                           unsigned long long* clocks, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
