@@ -466,3 +466,55 @@ def test_attention_splitkv_wrapper_rejects_bad_tensors():
         fa.attention_splitkv(q, kv, kv)  # CPU tensors
     with pytest.raises(ValueError):
         fa.attention_splitkv(q, kv, kv[:, :, :4])
+
+
+# ---------------------------------------------------------------------------
+# the matrix-core ceiling probe (include/fa2_probe.h, libfa2probe.so): a
+# measurement aid of its own library, not part of the attention ABI
+# ---------------------------------------------------------------------------
+PROBE_HEADER = os.path.join(ROOT, "include", "fa2_probe.h")
+
+
+def test_every_header_has_its_library():
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["fa2.h", "fa2_probe.h"]
+
+
+@pytest.fixture(scope="module")
+def probe():
+    from flashattention_tiled_amd.build import PROBE_LIB_PATH, build_probe
+
+    if not os.path.exists(PROBE_LIB_PATH):
+        build_probe(force=False)
+    import torch  # noqa: F401  (shares torch's HIP runtime)
+
+    p = ctypes.CDLL(PROBE_LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    p.fa2_probe_mfma_ceiling.argtypes = [vp, i, i, vp, vp, vp]
+    p.fa2_probe_mfma_ceiling.restype = i
+    p.fa2_probe_mfma_flops.argtypes = [i, i]
+    p.fa2_probe_mfma_flops.restype = ctypes.c_double
+    return p
+
+
+def test_probe_exports_exactly_its_header(probe):
+    from flashattention_tiled_amd.build import PROBE_LIB_PATH
+
+    text = open(PROBE_HEADER).read()
+    declared = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa2_\w+)\s*\(", text, flags=re.M)
+    assert sorted(declared) == ["fa2_probe_mfma_ceiling", "fa2_probe_mfma_flops"]
+    _, defined = _elf_dynamic(PROBE_LIB_PATH)
+    assert sorted(n for n in defined if n.startswith("fa2")) == sorted(declared)
+    for name in declared:
+        assert ctypes.cast(getattr(probe, name), ctypes.c_void_p).value
+
+
+def test_probe_flops_and_validation(probe):
+    # 4 waves x iters rounds x 16 products of 32 x 32 x 16 x 2 FLOPs per workgroup
+    assert probe.fa2_probe_mfma_flops(3, 5) == 3 * 4 * 5 * 16 * 32 * 32 * 16 * 2
+    fake = 1 << 20  # never dereferenced: validation returns first
+    assert probe.fa2_probe_mfma_ceiling(None, 1, 1, fake, fake, None) == 1
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, None, fake, None) == 1
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, None, None) == 1
+    assert probe.fa2_probe_mfma_ceiling(fake, 0, 1, fake, fake, None) == 2
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 0, fake, fake, None) == 2
