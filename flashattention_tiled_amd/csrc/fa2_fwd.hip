@@ -573,12 +573,13 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     tile_max<RB, NKB>(s_a, ce_a, m_run);
   }
 
-  // One pipeline step for tile j with parity PAR = j % 2 (known at compile
-  // time after unrolling by two); `cur` holds tile j's scores, `nxt` receives
+  // One pipeline step for tile j with parity PAR = j % 2 and ring stage
+  // SJ = j % NST (both known at compile time: the loop is unrolled by a
+  // multiple of 2 and of NST); `cur` holds tile j's scores, `nxt` receives
   // tile j + 1's.
-  auto step = [&](auto par, int j, f32x16 (&cur)[RB][NKB], float (&ce_cur)[RB],
+  auto step = [&](auto par, auto sj_c, int j, f32x16 (&cur)[RB][NKB], float (&ce_cur)[RB],
                   f32x16 (&nxt)[RB][NKB], float (&ce_nxt)[RB]) {
-    constexpr int PAR = decltype(par)::value;
+    constexpr int PAR = decltype(par)::value, SJ = decltype(sj_c)::value;
     uint32_t k_next, k_free, v_cur, v_free;  // K of tile j + 1, of tile j (done);
                                              // V of tile j, of tile j - 1 (done)
     if constexpr (NST == 2) {
@@ -587,11 +588,10 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
       v_cur = PAR ? kV1 : kV0;
       v_free = PAR ? kV0 : kV1;
     } else {
-      const int sj = wave_uniform(j % NST);  // stage of tile j
-      const int sn = sj + 1 == NST ? 0 : sj + 1, sp = sj == 0 ? NST - 1 : sj - 1;
+      constexpr int sn = (SJ + 1) % NST, sp = (SJ + NST - 1) % NST;
       k_next = kK0 + (uint32_t)(sn * TB);
-      k_free = kK0 + (uint32_t)(sj * TB);
-      v_cur = kV0 + (uint32_t)(sj * TB);
+      k_free = kK0 + (uint32_t)(SJ * TB);
+      v_cur = kV0 + (uint32_t)(SJ * TB);
       v_free = kV0 + (uint32_t)(sp * TB);
     }
     wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
@@ -622,10 +622,30 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
       for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
     }
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, s_a, ce_a, s_b, ce_b);
-    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1, s_b, ce_b, s_a, ce_a);
+  // unrolled by U steps, a multiple of 2 (score buffers) and of NST (stages)
+  constexpr int U = NST % 2 == 0 ? NST : 2 * NST;
+  auto step_u = [&](auto u, int j0) {
+    constexpr int UU = decltype(u)::value;
+    if constexpr (UU < U) {
+      if (UU == 0 || j0 + UU < n_tiles) {
+        if constexpr (UU % 2 == 0)
+          step(std::integral_constant<int, 0>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
+               s_a, ce_a, s_b, ce_b);
+        else
+          step(std::integral_constant<int, 1>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
+               s_b, ce_b, s_a, ce_a);
+      }
+    }
+  };
+  for (int j = 0; j < n_tiles; j += U) {
+    step_u(std::integral_constant<int, 0>{}, j);
+    step_u(std::integral_constant<int, 1>{}, j);
+    step_u(std::integral_constant<int, 2>{}, j);
+    step_u(std::integral_constant<int, 3>{}, j);
+    step_u(std::integral_constant<int, 4>{}, j);
+    step_u(std::integral_constant<int, 5>{}, j);
   }
+  static_assert(U <= 6, "unroll");
   // the last steps' loads (zeros into free stages) must land before the
   // workgroup's LDS is released
   wait_vm_lgkm0<0>();

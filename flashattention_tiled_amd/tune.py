@@ -44,7 +44,7 @@ CANDIDATES = {
     128: [(4, 1, 64, 2, 2), (4, 1, 64, 2, 0), (4, 1, 64, 2, 1), (4, 1, 64, 2, 4),
           (8, 1, 64, 2, 2), (4, 1, 32, 2, 0), (2, 1, 64, 2, 1), (4, 1, 128, 1, 2)],
     256: [(4, 1, 32, 1, 1, 4), (4, 1, 32, 1, 0), (4, 1, 32, 1, 1), (4, 1, 32, 1, 0, 4),
-          (4, 1, 32, 1, 2, 4), (4, 1, 32, 1, 1, 3), (4, 1, 32, 1, 1, 5), (8, 1, 32, 1, 0),
+          (4, 1, 32, 1, 2, 4), (4, 1, 32, 1, 1, 3), (8, 1, 32, 1, 0),
           (2, 1, 32, 1, 0)],
 }
 
@@ -58,7 +58,7 @@ def valid(D: int, cfg) -> bool:
             or w * 64 > 1024 or stages < 2):
         return False
     lpw = tile_bytes // 1024 // w
-    if (stages - 2) * 2 * lpw >= 64:
+    if (stages - 2) * 2 * lpw >= 64 or stages > 4:  # the key loop unrolls by at most 6
         return False
     ns1 = (D // 16) * (bc // 32)  # phase-1 k-steps per tile
     return le == 0 or (ns1 + le - 1) // le >= 2 * lpw

@@ -29,9 +29,11 @@ def test_validity_rule():
     # a tile must split into whole 1 KiB wave loads, and B_c into 32-key blocks
     assert not tune.valid(64, (16, 1, 32, 1, 0))
     assert not tune.valid(64, (4, 1, 48, 2, 0))
-    # ring depth: D = 256, 32-key tiles take 16 KiB per stage and ring, so five
-    # stages of K and V fill the 160 KiB; six do not
-    assert tune.valid(256, (4, 1, 32, 1, 1, 5))
+    # ring depth: D = 256, 32-key tiles take 16 KiB per stage and ring, so four
+    # stages of K and V take 128 KiB; six would exceed the 160 KiB, and five
+    # exceed the key loop's unroll (a multiple of 2 and of the depth, <= 6)
+    assert tune.valid(256, (4, 1, 32, 1, 1, 4))
+    assert not tune.valid(256, (4, 1, 32, 1, 1, 5))
     assert not tune.valid(256, (4, 1, 32, 1, 1, 6))
     assert not tune.valid(128, (4, 1, 64, 2, 2, 1))
 
