@@ -63,9 +63,9 @@ constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile
 // Iteration j reads K of tile j + 1 and V of tile j while K of tile
 // j + kStages and V of tile j + kStages - 1 load, so a tile's loads have
 // kStages - 1 iterations to land. Two stages fit two workgroups per compute
-// unit at D <= 128; D = 256 holds one workgroup per unit (its registers allow
-// one wave per SIMD), whose single wave per SIMD cannot hide a load behind
-// another workgroup's work, and it spends the spare LDS on a deeper ring.
+// unit at D <= 128. D = 256 holds one workgroup per unit (its registers allow
+// one wave per SIMD) and spends its LDS on 64-key tiles (2 x 2 x 32 KiB);
+// with 32-key tiles, four stages were best.
 // The defaults are the best of a sweep over these values on the benchmark
 // shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides one, as
 // "waves, row blocks, keys, waves per SIMD, load spacing[, stages]". D = 64 has
@@ -89,7 +89,7 @@ template <int W, int RB, int BC, int WPS, int LE, int NST = 2> struct TileCfg {
 #define FA2_TILE_D128 4, 1, 64, 2, 2
 #endif
 #ifndef FA2_TILE_D256
-#define FA2_TILE_D256 4, 1, 32, 1, 1, 4
+#define FA2_TILE_D256 4, 1, 64, 1, 1, 2
 #endif
 template <int D, bool LONG = false> struct Tile;
 template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};

@@ -43,9 +43,9 @@ CANDIDATES = {
          (4, 1, 128, 1, 0)],
     128: [(4, 1, 64, 2, 2), (4, 1, 64, 2, 0), (4, 1, 64, 2, 1), (4, 1, 64, 2, 4),
           (8, 1, 64, 2, 2), (4, 1, 32, 2, 0), (2, 1, 64, 2, 1), (4, 1, 128, 1, 2)],
-    256: [(4, 1, 32, 1, 1, 4), (4, 1, 32, 1, 0), (4, 1, 32, 1, 1), (4, 1, 32, 1, 0, 4),
-          (4, 1, 32, 1, 2, 4), (4, 1, 32, 1, 1, 3), (8, 1, 32, 1, 0),
-          (2, 1, 32, 1, 0)],
+    256: [(4, 1, 64, 1, 1, 2), (4, 1, 64, 1, 2, 2), (4, 1, 64, 1, 0, 2), (4, 1, 32, 1, 1, 4),
+          (4, 1, 32, 1, 0), (4, 1, 32, 1, 1), (4, 1, 32, 1, 0, 4), (4, 1, 32, 1, 2, 4),
+          (4, 1, 32, 1, 1, 3), (8, 1, 32, 1, 0), (2, 1, 32, 1, 0)],
 }
 
 
