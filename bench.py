@@ -328,10 +328,10 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, budget_s: float):
                 seconds=dt, parity_max_abs_o=o_err, parity_lse_rel=lse_err)
 
 
-def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20):
+def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20, dtype: str = "f16"):
     """Rate and clock of the matrix-core ceiling probe (libfa2probe.so): fp16
-    32x32x16 products on random N(0, 1) operands and nothing else, two
-    workgroups per compute unit, median of `launches` HIP-event timed
+    (or bf16) 32x32x16 products on random N(0, 1) operands and nothing else,
+    two workgroups per compute unit, median of `launches` HIP-event timed
     launches after `warmup_min_s` of warm-up. None when the probe is not
     built."""
     import ctypes
@@ -344,7 +344,7 @@ def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20):
         return None
     lib = ctypes.CDLL(PROBE_LIB_PATH)  # after torch: shares its HIP runtime
     vp, i = ctypes.c_void_p, ctypes.c_int
-    lib.fa2_probe_mfma_ceiling.argtypes = [vp, i, i, vp, vp, vp]
+    lib.fa2_probe_mfma_ceiling.argtypes = [vp, i, i, vp, vp, i, vp]
     lib.fa2_probe_mfma_ceiling.restype = i
     lib.fa2_probe_mfma_flops.argtypes = [i, i]
     lib.fa2_probe_mfma_flops.restype = ctypes.c_double
@@ -352,14 +352,15 @@ def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20):
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     n_wg, iters = 2 * n_cu, 4096
     g = torch.Generator("cpu").manual_seed(0)
-    ops = torch.randn(384 * 8, generator=g).to(torch.float16).to(dev)
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    ops = torch.randn(384 * 8, generator=g).to(tdt).to(dev)
     sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
     clocks = torch.zeros(n_wg * 4 * 2, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def launch():
         st = lib.fa2_probe_mfma_ceiling(ops.data_ptr(), n_wg, iters, sink.data_ptr(),
-                                        clocks.data_ptr(), stream)
+                                        clocks.data_ptr(), 0 if dtype == "f16" else 1, stream)
         if st != 0:
             raise RuntimeError(f"fa2_probe_mfma_ceiling status {st}")
 
@@ -381,7 +382,7 @@ def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20):
     ghz = float((ck[:, 0] / ck[:, 1]).mean()) * 0.1
     return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_TFLOPS, 4),
             "clock_ghz": round(ghz, 3), "workgroups": n_wg, "ms": round(med, 4),
-            "what": "fp16 32x32x16 matrix-core products on random N(0,1) operands only"}
+            "what": f"{dtype} 32x32x16 matrix-core products on random N(0,1) operands only"}
 
 
 def stats_line(w, r):
@@ -466,7 +467,8 @@ def main():
         run_table(args.table, args.steps, args.warmup)
         return
     if args.mfma_ceiling:
-        print(json.dumps(mfma_ceiling()), flush=True)
+        for dt in ("f16", "bf16"):
+            print(json.dumps(mfma_ceiling(dtype=dt)), flush=True)
         return
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -495,7 +497,7 @@ def main():
         log(f"[bench] oracle sample: {cpu['sample']}; parity max|dO|={cpu['parity_max_abs_o']:.3e} "
             f"lse_rel={cpu['parity_lse_rel']:.3e}")
 
-    ceiling = None if args.no_ceiling else mfma_ceiling()
+    ceiling = None if args.no_ceiling else mfma_ceiling(dtype=w.dtype)
     if ceiling is not None:
         ceiling["kernel_frac_of_probe"] = round(achieved / ceiling["tflops"], 4)
         log(f"[bench] matrix-core ceiling probe: {ceiling}")

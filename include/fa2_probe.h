@@ -1,5 +1,5 @@
 // Measurement aid beside the attention library (libfa2probe.so, a library of
-// its own): a kernel that does nothing but fp16 matrix-core products on
+// its own): a kernel that does nothing but fp16 or bf16 matrix-core products on
 // random operands, timed by the caller, to give the rate the matrix cores of
 // the GPU actually sustain on data like attention's. The nominal dense
 // fp16/bf16 peak of MI355X (256 CUs x 2.4 GHz x 4096 FLOP/clk/CU) assumes
@@ -14,18 +14,19 @@
 extern "C" {
 #endif
 
-// Number of 8 x fp16 operand vectors the kernel reads (6 per lane of a wave:
+// Number of 8 x 16-bit operand vectors the kernel reads (6 per lane of a wave:
 // 4 A and 2 B operands, rotated so that consecutive products see different
 // inputs).
 #define FA2_PROBE_OPERAND_VECTORS 384
 
 // FLOPs one launch performs: n_wg workgroups of 4 waves, each wave `iters`
-// rounds of 16 products of v_mfma_f32_32x32x16_f16 (32 x 32 x 16 x 2 FLOPs).
+// rounds of 16 products of a 32x32x16 matrix-core op (32 x 32 x 16 x 2 FLOPs).
 double fa2_probe_mfma_flops(int n_wg, int iters);
 
 // Enqueue one launch on `stream` (asynchronous, never synchronises).
-//   operands  device, FA2_PROBE_OPERAND_VECTORS x 8 fp16 values (16-byte
-//             aligned), read only; random N(0, 1) values model attention's
+//   operands  device, FA2_PROBE_OPERAND_VECTORS x 8 values of `dtype`
+//             (16-byte aligned), read only; random N(0, 1) values model
+//             attention's
 //   n_wg      workgroups (256 threads each; two fit on a compute unit)
 //   iters     rounds per wave, >= 1
 //   sink      device, n_wg x 256 floats: each thread writes one sum of its
@@ -33,10 +34,12 @@ double fa2_probe_mfma_flops(int n_wg, int iters);
 //   clocks    device, n_wg x 4 x 2 unsigned 64-bit values: per wave, the
 //             shader-clock ticks (s_memtime) and the constant 100 MHz
 //             reference ticks (s_memrealtime) its loop took
-// Returns 0, or 1 for a null pointer, 2 for n_wg < 1 or iters < 1, 8 when
-// the launch fails. The caller owns every buffer.
+//   dtype     0: fp16 operands (v_mfma_f32_32x32x16_f16), 1: bf16
+//             (v_mfma_f32_32x32x16_bf16), the codes of fa2.h's fa2_dtype
+// Returns 0, or 1 for a null pointer, 2 for n_wg < 1 or iters < 1, 4 for
+// another dtype, 8 when the launch fails. The caller owns every buffer.
 int fa2_probe_mfma_ceiling(const void* operands, int n_wg, int iters, float* sink,
-                           unsigned long long* clocks, hipStream_t stream);
+                           unsigned long long* clocks, int dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

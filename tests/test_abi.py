@@ -490,7 +490,7 @@ def probe():
 
     p = ctypes.CDLL(PROBE_LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
-    p.fa2_probe_mfma_ceiling.argtypes = [vp, i, i, vp, vp, vp]
+    p.fa2_probe_mfma_ceiling.argtypes = [vp, i, i, vp, vp, i, vp]
     p.fa2_probe_mfma_ceiling.restype = i
     p.fa2_probe_mfma_flops.argtypes = [i, i]
     p.fa2_probe_mfma_flops.restype = ctypes.c_double
@@ -513,8 +513,10 @@ def test_probe_flops_and_validation(probe):
     # 4 waves x iters rounds x 16 products of 32 x 32 x 16 x 2 FLOPs per workgroup
     assert probe.fa2_probe_mfma_flops(3, 5) == 3 * 4 * 5 * 16 * 32 * 32 * 16 * 2
     fake = 1 << 20  # never dereferenced: validation returns first
-    assert probe.fa2_probe_mfma_ceiling(None, 1, 1, fake, fake, None) == 1
-    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, None, fake, None) == 1
-    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, None, None) == 1
-    assert probe.fa2_probe_mfma_ceiling(fake, 0, 1, fake, fake, None) == 2
-    assert probe.fa2_probe_mfma_ceiling(fake, 1, 0, fake, fake, None) == 2
+    assert probe.fa2_probe_mfma_ceiling(None, 1, 1, fake, fake, 0, None) == 1
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, None, fake, 0, None) == 1
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, None, 0, None) == 1
+    assert probe.fa2_probe_mfma_ceiling(fake, 0, 1, fake, fake, 0, None) == 2
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 0, fake, fake, 1, None) == 2
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, fake, 2, None) == 4
+    assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, fake, -1, None) == 4

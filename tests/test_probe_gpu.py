@@ -8,8 +8,9 @@ import bench
 pytestmark = pytest.mark.gpu
 
 
-def test_ceiling_probe_rate_and_clock():
-    r = bench.mfma_ceiling(warmup_min_s=0.05, launches=3)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_ceiling_probe_rate_and_clock(dtype):
+    r = bench.mfma_ceiling(warmup_min_s=0.05, launches=3, dtype=dtype)
     assert r is not None, "libfa2probe.so is not built"
     print(f"[probe] {r}", flush=True)
     assert 0.5 <= r["clock_ghz"] <= 2.6
