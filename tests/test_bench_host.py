@@ -25,3 +25,17 @@ def test_traffic_null_for_other_sources_or_workload(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY",
                         _summary(tmp_path, bench.kernel_source_sha(), workload="other"))
     assert bench.read_traffic("sweep_s8192_d128") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU; --gpus N > 1 exits with a message (before
+    touching a device)."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
