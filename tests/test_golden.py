@@ -73,3 +73,48 @@ def test_gpu_matches_worked_example(causal, dtype):
     if causal:
         # row 0 sees key 0 alone: its output is V[0] exactly
         assert o[0, :2].tolist() == [1.0, 2.0]
+
+
+# The same instance read as decoding against a KV cache: the last Sq queries
+# of the sequence against all three keys, causal with the queries last (query
+# i of the Sq sits at position i + 3 - Sq and keeps keys j <= that position).
+# Its rows are the causal rows of the square instance.
+@pytest.mark.parametrize("sq", [1, 2])
+def test_oracle_kv_form_matches_worked_example(sq):
+    import oracle
+
+    g = _load()
+    exp = g["causal"]
+    q, k, v = _inputs(g, 2)
+    o, lse = oracle.attention_kv_f64(q[:, :, 3 - sq:], k, v, True, g["scale"])
+    assert np.abs(o[0, 0] - np.array(exp["o"][3 - sq:])).max() <= 1e-13
+    assert np.abs(lse[0, 0] - np.array(exp["lse"][3 - sq:])).max() <= 1e-13
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("sq", [1, 2])
+@pytest.mark.parametrize("kv", ["f16", "bf16", "e4m3"])
+@pytest.mark.parametrize("n_split", [1, 3])
+def test_gpu_splitkv_matches_worked_example(sq, kv, n_split):
+    import torch
+
+    import flashattention_tiled_amd as fa
+    from workloads import TOLERANCE_LSE_REL, TOLERANCE_O
+
+    g = _load()
+    exp = g["causal"]
+    qd = torch.bfloat16 if kv == "bf16" else torch.float16
+    q, k, v = (torch.from_numpy(a) for a in _inputs(g, 64))
+    q = q[:, :, 3 - sq:].to(qd).to("cuda:0")
+    # the integer inputs are exact in fp16, bf16 and e4m3 (descale 1)
+    kvd = torch.float8_e4m3fn if kv == "e4m3" else qd
+    k, v = k.to(kvd).to("cuda:0"), v.to(kvd).to("cuda:0")
+    o, lse = fa.attention_splitkv(q, k, v, causal=True, scale=g["scale"], n_split=n_split)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()[0, 0]
+    lse = lse.cpu().numpy()[0, 0].astype(np.float64)
+    dt = "bf16" if kv == "bf16" else "f16"
+    assert np.abs(o[:, :2] - np.array(exp["o"][3 - sq:])).max() <= TOLERANCE_O[dt]
+    assert (o[:, 2:] == 0).all()
+    ref = np.array(exp["lse"][3 - sq:])
+    assert (np.abs(lse - ref) / np.maximum(np.abs(ref), 1.0)).max() <= TOLERANCE_LSE_REL
