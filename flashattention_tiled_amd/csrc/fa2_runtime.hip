@@ -11,11 +11,6 @@
 
 namespace fa2_host {
 
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + nb && b0 < a0 + na;
-}
-
 namespace {
 
 // Per-device verdict on whether the device is gfx950 (0 unknown, 1 yes,
@@ -48,33 +43,6 @@ int check_device(int* n_cu) {
   return verdict == 1 ? FA2_OK : FA2_ERR_NO_DEVICE;
 }
 
-// Taking the dims of size > 1 in ascending stride order, each stride must
-// reach past the span of the dims before it.
-bool rows_disjoint(int B, int H, int S, int D, long long sb, long long sh, long long ss) {
-  long long n[3] = {B, H, S}, st[3] = {sb, sh, ss};
-  for (int i = 1; i < 3; ++i)
-    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
-      const long long tn = n[j], ts = st[j];
-      n[j] = n[j - 1];
-      st[j] = st[j - 1];
-      n[j - 1] = tn;
-      st[j - 1] = ts;
-    }
-  long long span = D;
-  for (int i = 0; i < 3; ++i) {
-    if (n[i] < 2) continue;
-    if (st[i] < span) return false;
-    span += st[i] * (n[i] - 1);
-  }
-  return true;
-}
-
-size_t extent_bytes(int B, int H, int S, int D, long long sb, long long sh, long long ss,
-                    int elem_bytes) {
-  return (size_t)(((long long)(B - 1) * sb + (long long)(H - 1) * sh + (long long)(S - 1) * ss +
-                   D) * elem_bytes);
-}
-
 }  // namespace fa2_host
 
 extern "C" int fa2_supported(int D, int dtype) {
@@ -91,7 +59,7 @@ extern "C" const char* fa2_status_string(int status) {
     case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA2_ERR_DTYPE: return "dtype must be FA2_F16 or FA2_BF16";
     case FA2_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";
-    case FA2_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA2_ERR_SCALE: return "scale must be finite (FP8 descales finite and > 0)";
     case FA2_ERR_NO_DEVICE: return "no current HIP device, or it is not a gfx950 (MI355X)";
     case FA2_ERR_LAUNCH: return "the HIP runtime reported an error at kernel launch";
     case FA2_ERR_ALIAS: return "o or lse overlaps q, k, v or each other (or the workspace overlaps any of them)";

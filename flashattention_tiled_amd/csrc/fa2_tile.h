@@ -248,7 +248,9 @@ __device__ __forceinline__ void tile_scores(const unsigned char* smem, uint32_t 
     }
 }
 
-// Each row's tile max of t = c_eff * (masked) scores.
+// Each row's tile max of t = c_eff * (masked) scores. The max is taken of
+// the products, so it holds for a negative c_eff as well (where it is c_eff
+// times the smallest score).
 template <int RB, int NKB>
 __device__ __forceinline__ void tile_max(const f32x16 (&acc)[RB][NKB], const float (&c_eff)[RB],
                                          float (&tmax)[RB]) {
@@ -258,8 +260,9 @@ __device__ __forceinline__ void tile_max(const f32x16 (&acc)[RB][NKB], const flo
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[rb][kb][r]), acc[rb][kb][r + 1]);
-    tmax[rb] = xor32_max(mx) * c_eff[rb];
+      for (int r = 0; r < 16; r += 2)
+        mx = fmaxf(fmaxf(mx, acc[rb][kb][r] * c_eff[rb]), acc[rb][kb][r + 1] * c_eff[rb]);
+    tmax[rb] = xor32_max(mx);
   }
 }
 

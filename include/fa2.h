@@ -49,7 +49,7 @@ typedef enum {
     FA2_ERR_HEADDIM = 3,   /* D is not 64, 128 or 256 */
     FA2_ERR_DTYPE = 4,     /* dtype is not FA2_F16 or FA2_BF16 */
     FA2_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
-    FA2_ERR_SCALE = 6,     /* scale is negative, NaN or infinite */
+    FA2_ERR_SCALE = 6,     /* scale is NaN or infinite (FP8: a descale not finite and > 0) */
     FA2_ERR_NO_DEVICE = 7, /* no current HIP device, or the device is not gfx950 */
     FA2_ERR_LAUNCH = 8,    /* the HIP runtime reported an error at launch */
     FA2_ERR_ALIAS = 9,     /* o or lse overlaps q, k or v, or o overlaps lse (split-KV:
@@ -76,8 +76,10 @@ typedef enum {
  * D        head dimension: 64, 128 or 256.
  * causal   nonzero: query i attends to keys j <= i (the diagonal is kept,
  *          so every row attends to at least key 0); zero: all keys.
- * scale    multiplies q . k before the mask and the softmax; finite and
- *          >= 0. Callers that want the usual default pass 1/sqrt(D).
+ * scale    multiplies q . k before the mask and the softmax; any finite
+ *          value (0 gives uniform weights, a negative one reverses the
+ *          order of the scores). Callers that want the usual default pass
+ *          1/sqrt(D).
  * dtype    FA2_F16 or FA2_BF16 (applies to q, k, v and o).
  * stream   a hipStream_t (NULL = the default stream) on the current device.
  *
@@ -162,15 +164,27 @@ int fa2_fwd_balanced(const void *q, const void *k, const void *v, void *o, float
  * when there is no usable device. */
 size_t fa2_fwd_balanced_workspace_bytes(int B, int H, int S, int D, int causal);
 
-/* 1 when fa2_fwd has a kernel for head dimension D and dtype, else 0. */
+/* 1 when fa2_fwd has a kernel for head dimension D and dtype, else 0: the
+ * head dims 64, 128 and 256 in fp16 or bf16, the support matrix jared-hpc
+ * Lecture 6 gives for FlashAttention-2 ("Use it in the real stack") and the
+ * infra.bea.ai guide's table ("When V2 Is Used vs Not": head dim up to
+ * 256). It lets a caller check a shape up front; the compute entry points
+ * refuse anything else on their own, with FA2_ERR_HEADDIM or FA2_ERR_DTYPE. */
 int fa2_supported(int D, int dtype);
 
-/* A static, human-readable description of a status code. */
+/* A static, human-readable description of a status code (never NULL; an
+ * unknown code gets a generic text). jared-hpc Lecture 6 ("Use it in the
+ * real stack") wants an input the kernel cannot serve to end in a visible
+ * error, never in a silent switch to another path; every entry point
+ * reports such a case as a nonzero status, and this text is what the
+ * caller shows for it. */
 const char *fa2_status_string(int status);
 
-/* Queries rows handled by one workgroup (the tile height along the query
+/* Query rows handled by one workgroup (the tile height B_r along the query
  * sequence) for head dimension D; 0 when D is unsupported. The launch grid
- * is (ceil(S / rows), H, B). */
+ * is (ceil(S / rows), H, B), the sequence-parallel grid of jared-hpc
+ * Lecture 6 ("FA2 change 1") and of the cookbook notebook's Triton launch
+ * (one program per (query block, batch * head)). */
 int fa2_rows_per_workgroup(int D);
 
 /*

@@ -152,7 +152,6 @@ _FWD_CASES = [
     (dict(lse=L + 2), fa.FA2_ERR_ALIGN),
     (dict(scale=float("nan")), fa.FA2_ERR_SCALE),
     (dict(scale=float("inf")), fa.FA2_ERR_SCALE),
-    (dict(scale=-0.5), fa.FA2_ERR_SCALE),
     (dict(o=Q), fa.FA2_ERR_ALIAS),
     (dict(o=K + 16), fa.FA2_ERR_ALIAS),
     (dict(lse=V + _N - 4), fa.FA2_ERR_ALIAS),
@@ -188,6 +187,21 @@ def test_no_device_status_without_gpu(lib):
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present; the fake pointers must not be launched on")
     assert _call() == fa.FA2_ERR_NO_DEVICE
+
+
+@pytest.mark.parametrize("scale", [-0.125, -1.0 / 64 ** 0.5, -0.0, -1e30])
+def test_negative_scale_is_valid(lib, scale):
+    """Any finite scale passes validation, negative ones included: the
+    prefill, key-split and split-KV calls all get as far as the device
+    lookup (no GPU here: FA2_ERR_NO_DEVICE)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call(scale=scale) == fa.FA2_ERR_NO_DEVICE
+    assert _call_strided(scale=scale) == fa.FA2_ERR_NO_DEVICE
+    assert _call_balanced(True, scale=scale) == fa.FA2_ERR_NO_DEVICE
+    assert _call_splitkv(scale=scale) == fa.FA2_ERR_NO_DEVICE
+    assert _call_splitkv_fp8(scale=scale) == fa.FA2_ERR_NO_DEVICE
 
 
 # ---------------------------------------------------------------------------

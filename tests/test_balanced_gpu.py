@@ -54,6 +54,21 @@ def test_split_matches_oracle(D, dtype, causal):
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
+def test_split_negative_scale(D):
+    """The key split with scale = -1/sqrt(D): each chunk's first-tile max is
+    taken in the scaled domain, so the merged rows meet the bar too."""
+    for causal in (True, False):
+        B, H, S = SPLIT[0]
+        what = f"balanced negative scale D={D} causal={causal} B={B} H={H} S={S}"
+        announce(what)
+        w = wl.Workload("bal", B, H, S, D, "f16", causal)
+        q, k, v = wl.make_qkv(w, seed=S + D + 1)
+        o, lse = _run(q, k, v, causal, -w.scale)
+        o_ref, lse_ref = oracle_full(q, k, v, causal, -w.scale)
+        assert_parity(o, lse, o_ref, lse_ref, "f16", what)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_unsplit_shapes_equal_fa2_fwd(D, causal):
     for B, H, S in UNSPLIT:

@@ -123,6 +123,40 @@ def test_scale_values():
         assert_parity(o, lse, o_ref, lse_ref, "f16", f"scale {scale}")
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_negative_scale(D, dtype):
+    """A negative scale (here -1/sqrt(D), and -3/sqrt(D) on peaky inputs)
+    reverses the order of the scores: the row max is then the scale times
+    the smallest dot product, which the kernel's first-tile max and its
+    rescale redo must both take in the scaled domain. Every output, causal
+    and not, ragged S over several tiles."""
+    for causal in (False, True):
+        for mult, S in ((1.0, 383), (3.0, 700)):
+            w = wl.Workload("neg", 1, 2, S, D, dtype, causal, qk_mult=mult)
+            scale = -mult / D ** 0.5
+            announce(f"negative scale {scale:.4f} {w}")
+            q, k, v = wl.make_qkv(w, seed=D + S)
+            o, lse = run_gpu(q, k, v, causal, scale)
+            o_ref, lse_ref = oracle_full(q, k, v, causal, scale)
+            assert_parity(o, lse, o_ref, lse_ref, dtype,
+                          f"scale {scale:.4f} D{D} {dtype} causal={causal} x{mult}")
+
+
+def test_negative_scale_falling_ramp():
+    """The ramp inputs above with a negative scale: the scores now climb
+    along the keys where the positive scale made them fall, forcing the
+    lazy reference max up tile after tile."""
+    for D in (64, 128, 256):
+        for causal in (False, True):
+            announce(f"negative-scale ramp D={D} causal={causal}")
+            q, k, v = _ramp_inputs(700, D, "f16", -1, seed=3 + D)
+            scale = -1.0 / D ** 0.5
+            o, lse = run_gpu(q, k, v, causal, scale)
+            o_ref, lse_ref = oracle_full(q, k, v, causal, scale)
+            assert_parity(o, lse, o_ref, lse_ref, "f16", f"neg ramp D{D} causal={causal}")
+
+
 # ---------------------------------------------------------------------------
 # the benchmark shapes at full size, sampled rows
 # ---------------------------------------------------------------------------

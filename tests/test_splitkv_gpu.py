@@ -51,6 +51,25 @@ def test_splitkv_shapes(D, dtype):
                 assert_parity(o, lse, o_ref, lse_ref, dtype, what)
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_splitkv_negative_scale(D, dtype):
+    """scale = -1/sqrt(D) (and -3/sqrt(D) with Q and K x3): every output
+    against the oracle, causal and not, several split counts."""
+    for mult in (1.0, 3.0):
+        for causal in (False, True):
+            for n_split in (1, 3, 0):
+                w = wl.DecodeWorkload("neg", 2, 2, 17, 700, D, dtype, causal, qk_mult=mult)
+                scale = -mult / D ** 0.5
+                what = (f"splitkv negative scale {scale:.4f} D={D} {dtype} causal={causal} "
+                        f"n_split={n_split}")
+                announce(what)
+                q, k, v = wl.make_qkv_decode(w, seed=D + n_split)
+                o, lse = _run(q, k, v, causal, scale, n_split)
+                o_ref, lse_ref = _oracle(q, k, v, causal, scale)
+                assert_parity(o, lse, o_ref, lse_ref, dtype, what)
+
+
 @pytest.mark.parametrize("w", wl.DECODE, ids=lambda w: w.name)
 def test_splitkv_benchmark_shapes(w):
     """The benchmark decoding shapes at full size, every output (the oracle
