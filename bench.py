@@ -6,7 +6,9 @@ resident in HBM). Default workload: B=2, H=16, S=8192, D=128, fp16, causal.
 Prints one JSON line on stdout; diagnostics go to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-    python bench.py --table PATH      # every benchmark shape: fa2_fwd, and fa2_fwd_balanced where it splits
+    python bench.py --table PATH [--oracle]   # every benchmark shape: fa2_fwd, and
+                                              # fa2_fwd_balanced where it splits; --oracle adds
+                                              # the fp64 oracle over every row (time, parity)
     python bench.py --decode-table PATH   # split-KV decode shapes, GB/s
     python bench.py --layer           # attention layer it/s and peak memory
     python bench.py --mfma-ceiling    # matrix-core rate and clock on random fp16 data
@@ -32,6 +34,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
+# Timing protocol of jared-hpc Lecture 6 ("Measure it"): at least 10 warm-up
+# launches before the timed ones; the GPU clock also needs some tenths of a
+# second of load to settle after idle, hence a time floor on the warm-up.
+WARMUP_MIN_LAUNCHES = 10
+WARMUP_MIN_S = 0.5
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fa2_fwd_kernel_sweep_s8192_d128_counters.md")
 
 
@@ -126,7 +133,7 @@ def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0, balanced: bo
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))  # ms
-    return dict(q=q, k=k, v=v, o=o, lse=lse, wall_s=wall, durs_ms=durs)
+    return dict(q=q, k=k, v=v, o=o, lse=lse, wall_s=wall, durs_ms=durs, launch=launch)
 
 
 def time_gpu_splitkv(w, steps: int, warmup_min_s: float):
@@ -385,6 +392,30 @@ def mfma_ceiling(warmup_min_s: float = 0.3, launches: int = 20, dtype: str = "f1
             "what": f"{dtype} 32x32x16 matrix-core products on random N(0,1) operands only"}
 
 
+def gpu_clock_mhz(launch, seconds: float):
+    """Median of the GPU clock readings (MHz, amdsmi through
+    torch.cuda.clock_rate) taken while `launch` keeps the GPU busy for
+    `seconds`; None when the clock cannot be read. amdsmi samples the clock
+    over periods of 1/6 s or more, so this is the steady-state clock of the
+    same launches, taken right after the timed ones."""
+    import torch
+
+    try:
+        torch.cuda.clock_rate(0)
+    except Exception as e:  # noqa: BLE001
+        log(f"[bench] GPU clock not readable: {e}")
+        return None
+    samples = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            launch()
+        samples.append(float(torch.cuda.clock_rate(0)))
+        torch.cuda.synchronize()
+    samples.sort()
+    return samples[len(samples) // 2] if samples else None
+
+
 def stats_line(w, r):
     durs = r["durs_ms"]
     avg = sum(durs) / len(durs)
@@ -392,11 +423,37 @@ def stats_line(w, r):
     return avg, med
 
 
-def run_table(path: str, steps: int, warmup: int):
+def oracle_full_leg(w, q, k, v, o_gpu, lse_gpu, threads: int):
+    """The fp64 oracle over every row of w on `threads` host threads: wall
+    seconds, GFLOP/s under the benchmark's FLOP count, and the parity of the
+    GPU output against it over all outputs."""
+    import numpy as np
+
+    import oracle
+
+    qn, kn, vn = (x.double().numpy() for x in (q, k, v))
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attention_f64(qn, kn, vn, w.causal, w.scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    og = o_gpu.cpu().double().numpy()
+    lg = lse_gpu.cpu().double().numpy()
+    o_err = float(np.abs(og - o_ref).max())
+    lse_err = float((np.abs(lg - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max())
+    return dict(seconds=dt, threads=threads, gflops=w.flops / dt / 1e9, max_abs_o=o_err,
+                lse_rel=lse_err)
+
+
+def run_table(path: str, steps: int, warmup: int, with_oracle: bool = False):
+    """Every benchmark shape through fa2_fwd (and fa2_fwd_balanced where it
+    splits the keys) into a CSV. with_oracle: also the fp64 oracle over every
+    row of each shape on all host cores (wall time, GFLOP/s, and the parity
+    of the fa2_fwd output against it), and the tiny shapes once more on one
+    thread."""
     import workloads as wl
 
     import flashattention_tiled_amd as fa
 
+    cores = len(os.sched_getaffinity(0))
     rows = []
     for w in wl.ALL:
         # fa2_fwd, and fa2_fwd_balanced where it splits the keys of this shape
@@ -411,12 +468,22 @@ def run_table(path: str, steps: int, warmup: int):
             line = (f"{w.name},{entry},{w.B},{w.H},{w.S},{w.D},{w.dtype},{int(w.causal)},"
                     f"{med:.4f},{avg:.4f},{min(r['durs_ms']):.4f},{tf:.1f},"
                     f"{100 * tf / PEAK_TFLOPS:.2f},{gbs:.1f}")
-            log(line)
-            rows.append(line)
+            if with_oracle:
+                legs = [oracle_full_leg(w, r["q"], r["k"], r["v"], r["o"], r["lse"], cores)]
+                if w in wl.TINY:
+                    legs.append(oracle_full_leg(w, r["q"], r["k"], r["v"], r["o"], r["lse"], 1))
+                for g in legs:
+                    rows.append(line + f",{g['threads']},{g['seconds']:.3f},{g['gflops']:.2f},"
+                                f"{g['max_abs_o']:.3e},{g['lse_rel']:.3e}")
+                    log(rows[-1])
+            else:
+                rows.append(line)
+                log(line)
             del r
     with open(path, "w") as f:
         f.write("workload,entry,B,H,S,D,dtype,causal,ms_median,ms_avg,ms_min,tflops,pct_peak,"
-                "alg_GBps\n")
+                "alg_GBps" + (",oracle_threads,oracle_s,oracle_GFLOPs,max_abs_o,lse_rel"
+                              if with_oracle else "") + "\n")
         f.write("\n".join(rows) + "\n")
 
 
@@ -429,6 +496,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--table", default=None, help="time every benchmark shape into a CSV")
+    ap.add_argument("--oracle", action="store_true",
+                    help="with --table: run the fp64 oracle over every row of each shape "
+                         "(wall time, GFLOP/s, parity of all outputs)")
     ap.add_argument("--layer", action="store_true",
                     help="time the attention layer against a score-materialising layer")
     ap.add_argument("--decode-table", default=None,
@@ -464,7 +534,7 @@ def main():
         run_decode_table(args.decode_table, args.steps)
         return
     if args.table:
-        run_table(args.table, args.steps, args.warmup)
+        run_table(args.table, args.steps, args.warmup, with_oracle=args.oracle)
         return
     if args.mfma_ceiling:
         for dt in ("f16", "bf16"):
@@ -482,13 +552,17 @@ def main():
 
     w = wl.by_name(args.workload)
     log(f"[bench] {w} steps={args.steps} warmup={args.warmup}")
-    r = time_gpu(w, args.steps, args.warmup)
+    # warm-up: the requested launches, at least WARMUP_MIN_LAUNCHES of them,
+    # then more until WARMUP_MIN_S of launches have run, so that the timed
+    # launches find the clock settled however short --warmup is
+    r = time_gpu(w, args.steps, max(args.warmup, WARMUP_MIN_LAUNCHES), warmup_min_s=WARMUP_MIN_S)
     avg, med = stats_line(w, r)
+    clock = gpu_clock_mhz(r.pop("launch"), 0.5)
     ms_per_step = 1e3 * r["wall_s"] / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (avg * 1e-3) / 1e12
     log(f"[bench] kernel avg {avg:.4f} ms, median {med:.4f} ms, min {r['durs_ms'][0]:.4f} ms, "
-        f"max {r['durs_ms'][-1]:.4f} ms; wall {ms_per_step:.4f} ms/step")
+        f"max {r['durs_ms'][-1]:.4f} ms; wall {ms_per_step:.4f} ms/step; clock {clock} MHz")
     traffic = read_traffic(w.name)
 
     cpu = None
@@ -529,6 +603,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic,
                      "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5),
+                     "kernel_ms_min": round(r["durs_ms"][0], 5),
+                     "kernel_ms_max": round(r["durs_ms"][-1], 5),
+                     "clock_mhz": clock,
+                     "warmup_floor": {"launches": WARMUP_MIN_LAUNCHES, "seconds": WARMUP_MIN_S},
                      "mfma_ceiling_probe": ceiling},
         "cpu_baseline": None if cpu is None else {
             k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
