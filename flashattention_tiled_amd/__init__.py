@@ -278,22 +278,27 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     B, H, S, D = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    # Tensors made here are allocated on the launch stream: torch's caching
+    # allocator then hands their memory to another allocation only in that
+    # stream's order, after the kernels that use it.
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        if lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     if out.shape != q.shape or out.dtype != q.dtype or out.stride(3) != 1:
         raise ValueError("out must be a tensor of q's shape and dtype with a contiguous last dim")
     if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, H, S) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, out))
     with torch.cuda.device(q.device):
         need = fa2_fwd_balanced_workspace_bytes(B, H, S, D, int(bool(causal))) if balanced else 0
         if need > 0:
             if workspace is None:
-                workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+                with torch.cuda.stream(stream):
+                    workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
             strides = None if contiguous else [x for t in (q, k, v, out) for x in t.stride()[:3]]
             status = fa2_fwd_balanced(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       lse.data_ptr(), B, H, S, D, strides, int(bool(causal)),
@@ -347,23 +352,26 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     Sk = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    if out is None:
-        out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    # allocated on the launch stream (see attention())
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(q, memory_format=torch.contiguous_format)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if out.shape != q.shape or out.dtype != q.dtype or out.stride(3) != 1:
         raise ValueError("out must be a tensor like q with a contiguous last dim")
     if lse.shape != (B, H, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (B, H, Sq) tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device)
     contiguous = all(t.is_contiguous() for t in (q, k, v, out))
     with torch.cuda.device(q.device):
         if n_split == 0:
             n_split = (fa2_splitkv_splits_fp8 if kv8 else fa2_splitkv_splits)(B, H, Sq, Sk)
         need = fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split)
         if workspace is None:
-            workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+            with torch.cuda.stream(stream):
+                workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
         ws_bytes = workspace.numel() * workspace.element_size()
         if not contiguous:
             strides = [x for t in (q, k, v, out) for x in t.stride()[:3]]

@@ -6,7 +6,7 @@ import torch
 
 import flashattention_tiled_amd as fa
 import workloads as wl
-from gpu_helpers import DEV, announce
+from gpu_helpers import DEV, announce, assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -101,6 +101,59 @@ def test_side_stream():
         o, lse = fa.attention(q, k, v, causal=True, scale=w.scale)
     s.synchronize()
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
+
+
+def test_explicit_stream_allocations():
+    """attention() and attention_splitkv() given a stream other than the
+    current one, on shapes whose partials go to a workspace the binding
+    allocates: that workspace (and O, lse) must come from the launch
+    stream's memory, so that allocations on the current stream made right
+    after the call cannot reuse it while the kernels still run. The launch
+    stream is kept busy first, the current stream then allocates and
+    overwrites blocks of the workspace's size throughout, and the results
+    must still match the oracle."""
+    import oracle
+
+    announce("explicit stream with a binding-allocated workspace")
+    s = torch.cuda.Stream()
+    busy = torch.randn(4096, 4096, device=DEV)
+    cases = []
+    # prefill with a key split (B=1, H=2, S=2048, D=128 causal splits)
+    w = wl.Workload("bal", 1, 2, 2048, 128, "f16", True)
+    assert fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, 1) > 0
+    q, k, v = wl.make_qkv(w, seed=21)
+    cases.append(("prefill", w, q, k, v))
+    dw = wl.DecodeWorkload("dec", 1, 4, 16, 4096, 128, "f16", True)
+    dq, dk, dv = wl.make_qkv_decode(dw, seed=22)
+    cases.append(("splitkv", dw, dq, dk, dv))
+    for kind, w, q, k, v in cases:
+        qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            for _ in range(8):
+                busy = busy @ busy
+                busy /= busy.abs().max()
+        if kind == "prefill":
+            need = fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, 1)
+            o, lse = fa.attention(qd, kd, vd, causal=True, scale=w.scale, stream=s)
+        else:
+            n = fa.fa2_splitkv_splits(w.B, w.H, w.Sq, w.Sk)
+            need = fa.fa2_splitkv_workspace_bytes(w.B, w.H, w.Sq, w.Sk, w.D, n)
+            o, lse = fa.attention_splitkv(qd, kd, vd, causal=True, scale=w.scale, stream=s)
+        # the current stream allocates and scribbles while the launch stream works
+        for _ in range(64):
+            junk = torch.empty((need,), dtype=torch.uint8, device=DEV)
+            junk.fill_(0x7F)
+            del junk
+        s.synchronize()
+        torch.cuda.synchronize()
+        if kind == "prefill":
+            o_ref, lse_ref = oracle.attention_f64(q.double().numpy(), k.double().numpy(),
+                                                  v.double().numpy(), True, w.scale)
+        else:
+            o_ref, lse_ref = oracle.attention_kv_f64(q.double().numpy(), k.double().numpy(),
+                                                     v.double().numpy(), True, w.scale)
+        assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, "f16", f"{kind} on a side stream")
 
 
 def test_unsupported_inputs_fail_loudly():
