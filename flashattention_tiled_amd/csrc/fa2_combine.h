@@ -21,17 +21,10 @@
 // start at or before the first row of the row's query tile).
 #pragma once
 
+#include "fa2_plan.h"
 #include "fa2_tile.h"
 
 namespace {
-
-size_t chunk_part_o_bytes(int B, int H, int Sr, int D, int n_split) {
-  const size_t b = (size_t)B * H * n_split * Sr * D * sizeof(float);
-  return (b + 255) / 256 * 256;
-}
-size_t chunk_workspace_bytes(int B, int H, int Sr, int D, int n_split) {
-  return chunk_part_o_bytes(B, H, Sr, D, n_split) + (size_t)B * H * n_split * Sr * 3 * sizeof(float);
-}
 
 // One wave per row, D / 64 columns per lane. The chunks' (m, l, l') are
 // read 64 at a time, one chunk per lane, and reduced across the wave; the

@@ -25,6 +25,7 @@
 // fa2_combine.h for all Sq rows (row0 = 0); part_ml starts at the part_o
 // size rounded up to 256 bytes.
 
+#include "fa2_plan.h"
 #include "fa2_tile.h"
 #include "fa2_host.h"
 #include "fa2_combine.h"
@@ -35,17 +36,6 @@ using fa2_host::overlaps;
 using fa2_host::rows_disjoint;
 
 namespace {
-
-// KV8: K and V hold FP8 e4m3 codes (one byte per element) instead of 16-bit
-// values.
-template <int D, bool KV8 = false> struct SplitTile {
-  static constexpr int kBc = 32;
-  static constexpr int kTileBytes = kBc * D * (KV8 ? 1 : 2);
-  static constexpr int kLoadsPerWave = kTileBytes / 1024;  // one wave loads the whole tile
-  static constexpr int kLdsBytes = 4 * kTileBytes;         // K and V, two stages each
-  static_assert(kTileBytes % 1024 == 0, "a tile is whole 1 KiB wave loads");
-};
-
 
 // ---- FP8 (e4m3) K and V ------------------------------------------------
 // Codes (OCP FP8 e4m3: sign, 4 exponent bits of bias 7, 3 mantissa bits)
@@ -374,23 +364,6 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   }
 }
 
-// Key chunks per (b, h) for a launch: enough workgroups for about two on
-// every compute unit with 16-bit K and V, four with FP8 (a chunk then holds
-// half the bytes, and the code conversions want more waves beside the
-// loads), each chunk at least 4 tiles long. Measured on decode shapes: more,
-// shorter chunks lose bandwidth.
-int splitkv_default_splits(int B, int H, int Sq, int Sk, int n_cu, bool kv8) {
-  const long long n_qblk = (Sq + 31) / 32;
-  const long long n_tiles = (Sk + SplitTile<64>::kBc - 1) / SplitTile<64>::kBc;
-  const long long target = (kv8 ? 4LL : 2LL) * n_cu;
-  long long want = (target + (long long)B * H * n_qblk - 1) / ((long long)B * H * n_qblk);
-  const long long cap = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
-  if (want > cap) want = cap;
-  if (want < 1) want = 1;
-  if (want > 1024) want = 1024;
-  return (int)want;
-}
-
 // Launch the partial and combine kernels. kv8: K and V are FP8 codes with
 // these descales (k_mult, v_mult), else 16-bit values (both 1).
 template <int D, int DT, bool CAUSAL, bool KV8>
@@ -399,9 +372,8 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v, void* o, 
                           const SkvStrides& st, int n_split, void* ws, hipStream_t stream) {
   using ST = SplitTile<D, KV8>;
   // chunks of whole tiles; trailing splits that would be empty are dropped
-  const int n_tiles = (Sk + ST::kBc - 1) / ST::kBc;
-  const int chunk_tiles = (n_tiles + n_split - 1) / n_split;
-  const int n_eff = (n_tiles + chunk_tiles - 1) / chunk_tiles;
+  int chunk_tiles = 0, n_eff = 0;
+  splitkv_chunking(Sk, ST::kBc, n_split, chunk_tiles, n_eff);
   const int n_qblk = (Sq + 31) / 32;
   float* part_o = (float*)ws;
   float* part_ml = (float*)((char*)ws + chunk_part_o_bytes(B, H, Sq, D, n_eff));
@@ -494,7 +466,7 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
   if (strides && !rows_disjoint(B, H, Sq, D, st.ob, st.oh, st.os)) return FA2_ERR_STRIDE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;
-  if (!std::isfinite(scale) || scale < 0.f) return FA2_ERR_SCALE;
+  if (!std::isfinite(scale)) return FA2_ERR_SCALE;
   if (!std::isfinite(k_descale) || !(k_descale > 0.f) || !std::isfinite(v_descale) ||
       !(v_descale > 0.f))
     return FA2_ERR_SCALE;

@@ -5,7 +5,7 @@ Each candidate sets one head dim's tile configuration (waves per workgroup,
 32-row blocks per wave, keys per tile, waves per SIMD, load spacing and,
 optionally, the depth of the K and V LDS rings (2 if absent); so
 B_r = 32 * waves * row blocks and B_c = keys per tile) through the
-FA2_TILE_D<D> macro of csrc/fa2_fwd.hip and is built into a library of its
+FA2_TILE_D<D> macro of csrc/fa2_plan.h and is built into a library of its
 own (without the library's switch to its long-sequence D = 64 tile, so that
 the candidate itself runs at every length). On a GPU, every library runs every
 benchmark shape of its head dim in

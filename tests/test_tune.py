@@ -7,7 +7,7 @@ import re
 from flashattention_tiled_amd import tune
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "flashattention_tiled_amd", "csrc", "fa2_fwd.hip")
+                   "flashattention_tiled_amd", "csrc", "fa2_plan.h")
 
 
 def test_first_candidate_is_the_library_default():
