@@ -24,6 +24,8 @@ C entry points, re-exported under the same names:
     fa2_fwd_splitkv_strided(q, k, v, o, lse, B, H, Sq, Sk, D, strides, causal,
                             scale, dtype, kv_fp8, k_descale, v_descale, n_split,
                             workspace, workspace_bytes, stream) -> int
+    fa2_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype,
+                            n_split, stream) -> int   (no workspace, allocates nothing)
     fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) -> int
     fa2_splitkv_splits(B, H, Sq, Sk) -> int
     fa2_splitkv_splits_fp8(B, H, Sq, Sk) -> int
@@ -59,11 +61,12 @@ FA2_ERR_LAUNCH = 8
 FA2_ERR_ALIAS = 9
 FA2_ERR_WORKSPACE = 10
 FA2_ERR_STRIDE = 11
+FA2_ERR_SCRATCH = 12
 
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_fwd_balanced",
                     "fa2_fwd_balanced_workspace_bytes", "fa2_supported", "fa2_status_string",
                     "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_fwd_splitkv_fp8",
-                    "fa2_fwd_splitkv_strided",
+                    "fa2_fwd_splitkv_strided", "fa2_fwd_splitkv_noalloc",
                     "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits",
                     "fa2_splitkv_splits_fp8")
 
@@ -139,6 +142,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_longlong), i, f, i, i, f, f,
                                             i, vp, sz, vp]
     lib.fa2_fwd_splitkv_strided.restype = i
+    lib.fa2_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa2_fwd_splitkv_noalloc.restype = i
     lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa2_splitkv_workspace_bytes.restype = sz
     lib.fa2_splitkv_splits.argtypes = [i, i, i, i]
@@ -222,6 +227,16 @@ def fa2_fwd_splitkv_strided(q: int, k: int, v: int, o: int, lse: int, B: int, H:
         q, k, v, o, lse, B, H, Sq, Sk, D, st, int(causal), float(scale), int(dtype), int(kv_fp8),
         float(k_descale), float(v_descale), int(n_split), workspace, int(workspace_bytes),
         stream))
+
+
+def fa2_fwd_splitkv_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int,
+                            Sk: int, D: int, causal: int, scale: float, dtype: int, n_split: int,
+                            stream: int) -> int:
+    """Direct call of the split-KV entry point that allocates nothing (its
+    partials go to the library's fixed scratch); returns the status."""
+    return int(load_library().fa2_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D,
+                                                      int(causal), float(scale), int(dtype),
+                                                      int(n_split), stream))
 
 
 def fa2_splitkv_workspace_bytes(B: int, H: int, Sq: int, Sk: int, D: int, n_split: int) -> int:

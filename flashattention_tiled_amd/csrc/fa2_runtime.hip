@@ -66,6 +66,9 @@ extern "C" const char* fa2_status_string(int status) {
     case FA2_ERR_STRIDE:
       return "strides must be in [0, 2^40] and multiples of 8, sequence strides >= D, and o's "
              "rows must not overlap";
+    case FA2_ERR_SCRATCH:
+      return "the call needs more scratch than the no-allocation entry point's fixed "
+             "FA2_SCRATCH_BYTES; pass a workspace to fa2_fwd_splitkv instead";
     case FA2_ERR_WORKSPACE:
       return "the workspace is NULL, not 16-byte aligned, or smaller than fa2_splitkv_workspace_bytes";
     default: return "unknown fa2 status";

@@ -25,6 +25,8 @@
 // fa2_combine.h for all Sq rows (row0 = 0); part_ml starts at the part_o
 // size rounded up to 256 bytes.
 
+#include <mutex>
+
 #include "fa2_plan.h"
 #include "fa2_tile.h"
 #include "fa2_host.h"
@@ -428,13 +430,52 @@ hipError_t launch_splitkv_any(int D, int dtype, int causal, const void* q, const
   }
 }
 
+}  // namespace
+
+// Scratch of fa2_fwd_splitkv_noalloc: the chunk partials of calls that
+// bring no workspace. The library's code object holds one copy per GPU it
+// is loaded on, for the life of the process. In host code `scratch` names a
+// host-side stand-in, never the device memory: scratch_here() looks up the
+// current device's address once and every launch takes that pointer.
+static __device__ __align__(256) unsigned char scratch[FA2_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices] = {};
+
+// The current device's copy of `scratch` (FA2_OK), found by
+// hipGetSymbolAddress on the first call on that device.
+int scratch_here(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return FA2_ERR_NO_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FA2_ERR_LAUNCH;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return FA2_OK;
+}
+
 // Checks shared by the split-KV entry points, in the documented order, and
 // the launch. kv_elem_bytes: 2 for 16-bit K and V, 1 for FP8. strides:
-// nullptr for contiguous tensors, else 12 element strides.
+// nullptr for contiguous tensors, else 12 element strides. use_scratch: the
+// partials go to the library's scratch (no workspace is passed; a call
+// that needs more than FA2_SCRATCH_BYTES is refused).
 int splitkv_call(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int Sq, int Sk, int D, const long long* strides, int causal, float scale,
                  int dtype, float k_descale, float v_descale, int kv_elem_bytes, int n_split,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 void* workspace, size_t workspace_bytes, void* stream,
+                 bool use_scratch = false) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || B > 65535 || H > 65535 || n_split < 0)
     return FA2_ERR_SHAPE;
@@ -482,6 +523,17 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
   }
   if (n_split > 65536) return FA2_ERR_SHAPE;
   const size_t need = chunk_workspace_bytes(B, H, Sq, D, n_split);
+  if (use_scratch) {
+    if (need > (size_t)FA2_SCRATCH_BYTES) return FA2_ERR_SCRATCH;
+    if (!device_checked) {
+      const int dev = check_device(&n_cu);
+      if (dev != FA2_OK) return dev;
+      device_checked = true;
+    }
+    const int got = scratch_here(&workspace);
+    if (got != FA2_OK) return got;
+    workspace_bytes = FA2_SCRATCH_BYTES;
+  }
   if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < need) return FA2_ERR_WORKSPACE;
   // overlap, by the byte range each tensor spans
   const size_t q_bytes = extent_bytes(B, H, Sq, D, st.qb, st.qh, st.qs, 2);
@@ -546,6 +598,13 @@ extern "C" int fa2_fwd_splitkv(const void* q, const void* k, const void* v, void
                                void* stream) {
   return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, nullptr, causal, scale, dtype, 1.f, 1.f, 2,
                       n_split, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa2_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int H, int Sq, int Sk, int D, int causal,
+                                       float scale, int dtype, int n_split, void* stream) {
+  return splitkv_call(q, k, v, o, lse, B, H, Sq, Sk, D, nullptr, causal, scale, dtype, 1.f, 1.f, 2,
+                      n_split, nullptr, 0, stream, true);
 }
 
 extern "C" int fa2_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o,

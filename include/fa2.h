@@ -55,8 +55,10 @@ typedef enum {
     FA2_ERR_ALIAS = 9,     /* o or lse overlaps q, k or v, or o overlaps lse (split-KV:
                               or the workspace overlaps any tensor) */
     FA2_ERR_WORKSPACE = 10, /* split-KV: workspace NULL, misaligned or too small */
-    FA2_ERR_STRIDE = 11     /* strided: a stride negative, above 2^40 or not a multiple of 8,
+    FA2_ERR_STRIDE = 11,    /* strided: a stride negative, above 2^40 or not a multiple of 8,
                                a sequence stride below D, or o's rows overlapping */
+    FA2_ERR_SCRATCH = 12    /* no-allocation split-KV: the call needs more scratch than the
+                               library's fixed FA2_SCRATCH_BYTES */
 } fa2_status;
 
 /*
@@ -276,6 +278,34 @@ int fa2_fwd_splitkv_strided(const void *q, const void *k, const void *v, void *o
                             int causal, float scale, int dtype, int kv_fp8, float k_descale,
                             float v_descale, int n_split, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/*
+ * fa2_fwd_splitkv_noalloc -- fa2_fwd_splitkv for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc. It takes no workspace: the partial
+ * results of the key chunks go to a scratch array the library holds in
+ * device memory for the life of the process, FA2_SCRATCH_BYTES on every GPU
+ * it runs on. The call allocates nothing (no hipMalloc, no allocating
+ * library routine); on its first call on a device it looks up that
+ * device's copy of the array.
+ *
+ * Arguments, arithmetic, kernels and result are those of fa2_fwd_splitkv
+ * with the same n_split (0: the library's default), bit for bit.
+ * Returns FA2_ERR_SCRATCH, before anything is launched, when
+ * fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) for the split count
+ * the call takes exceeds FA2_SCRATCH_BYTES; otherwise the codes of
+ * fa2_fwd_splitkv (never FA2_ERR_WORKSPACE).
+ *
+ * Every call on one GPU shares that GPU's scratch, and the array keeps the
+ * last call's partials (nothing in it needs to start at zero: every
+ * partial the merge reads is written first by the same call). Calls that
+ * overlap in time on one GPU -- on two streams, or from two threads
+ * without ordering -- race on it; order them on one stream.
+ */
+#define FA2_SCRATCH_BYTES (16u << 20)
+int fa2_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                            int B, int H, int Sq, int Sk, int D, int causal, float scale,
+                            int dtype, int n_split, void *stream);
 
 /* Bytes of workspace fa2_fwd_splitkv and fa2_fwd_splitkv_fp8 need for these
  * sizes and n_split; n_split = 0 gives enough for the default split count

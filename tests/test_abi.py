@@ -379,6 +379,43 @@ def test_splitkv_validation_status(lib, kw, status):
     assert _call_splitkv(**kw) == status
 
 
+def _call_splitkv_noalloc(**kw):
+    args = dict(q=QS, k=KS, v=VS, o=OS, lse=LS, B=1, H=1, Sq=_SQ, Sk=_SK, D=_D, causal=0,
+                scale=0.125, dtype=fa.FA2_F16, n_split=4, stream=None)
+    args.update(kw)
+    return fa.fa2_fwd_splitkv_noalloc(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA2_ERR_NULL),
+    (dict(Sq=0), fa.FA2_ERR_SHAPE),
+    (dict(causal=1, Sq=_SK + 1), fa.FA2_ERR_SHAPE),
+    (dict(n_split=-1), fa.FA2_ERR_SHAPE),
+    (dict(D=96), fa.FA2_ERR_HEADDIM),
+    (dict(dtype=2), fa.FA2_ERR_DTYPE),
+    (dict(k=KS + 8), fa.FA2_ERR_ALIGN),
+    (dict(scale=float("nan")), fa.FA2_ERR_SCALE),
+    # 64 x 64 heads x 8 chunks x 64 rows x (256 + 3) floats: far past the scratch
+    (dict(B=64, H=64, Sq=64, Sk=4096, D=256, n_split=8), fa.FA2_ERR_SCRATCH),
+    # just past it: 1 x 1 x n chunks x 4 rows x 67 floats > 16 MiB
+    (dict(n_split=(16 << 20) // (4 * 67 * 4) + 1), fa.FA2_ERR_SCRATCH),
+])
+def test_splitkv_noalloc_validation(lib, kw, status):
+    """The no-allocation split-KV call checks its arguments as fa2_fwd_splitkv
+    does, and refuses a call whose partials need more than the fixed scratch
+    before it looks at the device."""
+    assert _call_splitkv_noalloc(**kw) == status
+
+
+def test_splitkv_noalloc_reaches_device(lib):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    assert _call_splitkv_noalloc() == fa.FA2_ERR_NO_DEVICE
+    assert _call_splitkv_noalloc(n_split=0) == fa.FA2_ERR_NO_DEVICE
+    assert "scratch" in fa.fa2_status_string(fa.FA2_ERR_SCRATCH)
+
+
 def _call_splitkv_fp8(**kw):
     args = dict(q=QS, k=KS, v=VS, o=OS, lse=LS, B=1, H=1, Sq=_SQ, Sk=_SK, D=_D, causal=0,
                 scale=0.125, k_descale=0.01, v_descale=0.02, dtype=fa.FA2_F16, n_split=4,
