@@ -24,6 +24,8 @@ C entry points, re-exported under the same names:
     fa2_fwd_splitkv_strided(q, k, v, o, lse, B, H, Sq, Sk, D, strides, causal,
                             scale, dtype, kv_fp8, k_descale, v_descale, n_split,
                             workspace, workspace_bytes, stream) -> int
+    fa2_fwd_fp8(q, k, v, o, lse, B, H, S, D, causal, scale, q_descale, k_descale,
+                v_descale, dtype, stream) -> int   (e4m3 q, k, v; fp16/bf16 o)
     fa2_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, causal, scale, dtype,
                             n_split, stream) -> int   (no workspace, allocates nothing)
     fa2_splitkv_workspace_bytes(B, H, Sq, Sk, D, n_split) -> int
@@ -66,7 +68,7 @@ FA2_ERR_SCRATCH = 12
 EXPORTED_SYMBOLS = ("fa2_fwd", "fa2_fwd_strided", "fa2_fwd_balanced",
                     "fa2_fwd_balanced_workspace_bytes", "fa2_supported", "fa2_status_string",
                     "fa2_rows_per_workgroup", "fa2_fwd_splitkv", "fa2_fwd_splitkv_fp8",
-                    "fa2_fwd_splitkv_strided", "fa2_fwd_splitkv_noalloc",
+                    "fa2_fwd_splitkv_strided", "fa2_fwd_splitkv_noalloc", "fa2_fwd_fp8",
                     "fa2_splitkv_workspace_bytes", "fa2_splitkv_splits",
                     "fa2_splitkv_splits_fp8")
 
@@ -142,6 +144,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.POINTER(ctypes.c_longlong), i, f, i, i, f, f,
                                             i, vp, sz, vp]
     lib.fa2_fwd_splitkv_strided.restype = i
+    lib.fa2_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, i, vp]
+    lib.fa2_fwd_fp8.restype = i
     lib.fa2_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa2_fwd_splitkv_noalloc.restype = i
     lib.fa2_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -227,6 +231,59 @@ def fa2_fwd_splitkv_strided(q: int, k: int, v: int, o: int, lse: int, B: int, H:
         q, k, v, o, lse, B, H, Sq, Sk, D, st, int(causal), float(scale), int(dtype), int(kv_fp8),
         float(k_descale), float(v_descale), int(n_split), workspace, int(workspace_bytes),
         stream))
+
+
+def fa2_fwd_fp8(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, S: int, D: int,
+                causal: int, scale: float, q_descale: float, k_descale: float, v_descale: float,
+                dtype: int, stream: int) -> int:
+    """Direct call of the FP8 (e4m3 Q, K, V) prefill entry point; returns the status."""
+    return int(load_library().fa2_fwd_fp8(q, k, v, o, lse, B, H, S, D, int(causal), float(scale),
+                                          float(q_descale), float(k_descale), float(v_descale),
+                                          int(dtype), stream))
+
+
+def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None,
+                  q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
+                  out_dtype=None, out=None, lse=None, stream=None):
+    """O, lse of attention over FP8 inputs: q, k, v are contiguous (B, H, S,
+    D) torch.float8_e4m3fn CUDA tensors whose values are codes times the
+    descales; O is fp16 (default) or bf16 (`out_dtype`), lse (B, H, S)
+    float32. Runs fa2_fwd_fp8 on `stream` (default: torch's current stream)
+    without synchronising. Raises FA2Error on any nonzero status."""
+    import torch
+
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    if fp8 is None or not (q.dtype == k.dtype == v.dtype == fp8):
+        raise ValueError("q, k and v must be torch.float8_e4m3fn tensors")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one (B, H, S, D) shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    out_dtype = out_dtype or torch.float16
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty((B, H, S, D), dtype=out_dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (B, H, S) tensor")
+    with torch.cuda.device(q.device):
+        status = fa2_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, S, D, int(bool(causal)), float(scale),
+                             float(q_descale), float(k_descale), float(v_descale),
+                             _dtype_code(out), stream.cuda_stream)
+    if status != FA2_OK:
+        raise FA2Error(status, fa2_status_string(status))
+    return out, lse
 
 
 def fa2_fwd_splitkv_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, Sq: int,

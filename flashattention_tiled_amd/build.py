@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 # the parts of the library, compiled as the one translation unit fa2_lib.hip
 PARTS = [os.path.join(CSRC, f) for f in
          ("fa2_lib.hip", "fa2_runtime.hip", "fa2_fwd.hip", "fa2_splitkv.hip", "fa2_tile.h",
-          "fa2_host.h", "fa2_combine.h", "fa2_plan.h")]
+          "fa2_host.h", "fa2_combine.h", "fa2_plan.h", "fa2_fwd_fp8.hip")]
 SOURCES = [os.path.join(CSRC, "fa2_lib.hip")]
 # the files that hold the prefill kernel's (fa2_fwd_kernel's) code
 PREFILL_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("fa2_plan.h", "fa2_tile.h", "fa2_fwd.hip")]

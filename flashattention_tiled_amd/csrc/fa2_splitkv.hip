@@ -63,40 +63,6 @@ __device__ __forceinline__ u32x4 e4m3x8_op(uint32_t x0, uint32_t x1) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// 16-byte chunk swizzles of FP8 tiles (rows of D bytes, D / 16 chunks).
-// K is read 16 bytes per lane, 16 lanes (rows 0-15 or 16-31 of a key block)
-// per cycle: XOR by the row bits above those that already separate rows in
-// the 64 banks. V is read by ds_read_b64_tr_b8, 32 lanes per cycle over 8
-// rows x 2 chunks; an even XOR keeps a chunk pair together and gives each
-// of the 4 rows of one parity (D = 64: of the 2 rows of one residue mod 4;
-// D = 256: each of the 8 rows) its own pair.
-template <int D>
-__device__ __forceinline__ int swz_k8(int row) {
-  return D == 64 ? (row >> 2) & 3 : D == 128 ? (row >> 1) & 7 : row & 15;
-}
-template <int D>
-__device__ __forceinline__ int swz_v8(int row) {
-  return D == 64    ? ((row >> 3) & 1) << 1
-         : D == 128 ? (((row >> 1) & 1) | ((row >> 2) & 2)) << 1
-                    : ((row & 3) | ((row >> 1) & 4)) << 1;
-}
-
-// Per-lane byte offsets of the 16-byte chunks a one-wave FP8 tile load
-// fetches from key rows `row_bytes` apart: LDS slot p of the tile receives
-// chunk (p % (D/16)) ^ swz(row) of key row p / (D/16).
-template <int D, int LPW, bool IS_V>
-__device__ __forceinline__ void tile_load_offsets8(int lane, uint32_t row_bytes,
-                                                   uint32_t (&off)[LPW]) {
-  constexpr int CPR = D / 16;
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int p = i * 64 + lane;
-    const int r = p / CPR, cp = p % CPR;
-    const int c = cp ^ (IS_V ? swz_v8<D>(r) : swz_k8<D>(r));
-    off[i] = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
-  }
-}
-
 // S^T = K_t Q^T for an FP8 K tile at byte k_stage: each 16-byte read of row
 // 32 kb + l32 (chunk 2 u + hi) gives the K operands of k-steps 2 u and
 // 2 u + 1, so k-step 2 u + v covers dims 32 u + 16 hi + 8 v .. + 7, the
@@ -264,8 +230,8 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   const unsigned char* v_head = (const unsigned char*)v + (size_t)(b * st.vb + h * st.vh) * EB;
   uint32_t k_off[LPW], v_off[LPW];
   if constexpr (KV8) {
-    tile_load_offsets8<D, LPW, false>(lane, k_rb, k_off);
-    tile_load_offsets8<D, LPW, true>(lane, v_rb, v_off);
+    tile_load_offsets8<D, LPW, false>(0, lane, k_rb, k_off);
+    tile_load_offsets8<D, LPW, true>(0, lane, v_rb, v_off);
   } else {
     tile_load_offsets_strided<D, LPW, false>(0, lane, k_rb, k_off);
     tile_load_offsets_strided<D, LPW, true>(0, lane, v_rb, v_off);

@@ -117,6 +117,41 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 64 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
 }
 
+// 16-byte chunk swizzles of FP8 tiles (rows of D bytes, D / 16 chunks).
+// K is read 16 bytes per lane, 16 lanes (rows 0-15 or 16-31 of a key block)
+// per cycle: XOR by the row bits above those that already separate rows in
+// the 64 banks. V is read by ds_read_b64_tr_b8, 32 lanes per cycle over 8
+// rows x 2 chunks; an even XOR keeps a chunk pair together and gives each
+// of the 4 rows of one parity (D = 64: of the 2 rows of one residue mod 4;
+// D = 256: each of the 8 rows) its own pair.
+template <int D>
+__device__ __forceinline__ int swz_k8(int row) {
+  return D == 64 ? (row >> 2) & 3 : D == 128 ? (row >> 1) & 7 : row & 15;
+}
+template <int D>
+__device__ __forceinline__ int swz_v8(int row) {
+  return D == 64    ? ((row >> 3) & 1) << 1
+         : D == 128 ? (((row >> 1) & 1) | ((row >> 2) & 2)) << 1
+                    : ((row & 3) | ((row >> 1) & 4)) << 1;
+}
+
+// Per-lane byte offsets of the 16-byte chunks this wave's share of an FP8
+// tile load fetches from key rows `row_bytes` apart: LDS slot
+// p = (wave * LPW + i) * 64 + lane of the tile receives chunk
+// (p % (D/16)) ^ swz(row) of key row p / (D/16).
+template <int D, int LPW, bool IS_V>
+__device__ __forceinline__ void tile_load_offsets8(int wave, int lane, uint32_t row_bytes,
+                                                   uint32_t (&off)[LPW]) {
+  constexpr int CPR = D / 16;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int p = (wave * LPW + i) * 64 + lane;
+    const int r = p / CPR, cp = p % CPR;
+    const int c = cp ^ (IS_V ? swz_v8<D>(r) : swz_k8<D>(r));
+    off[i] = (uint32_t)r * row_bytes + (uint32_t)(c * 16);
+  }
+}
+
 // s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding; expcnt not waited).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {

@@ -307,6 +307,36 @@ int fa2_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o
                             int B, int H, int Sq, int Sk, int D, int causal, float scale,
                             int dtype, int n_split, void *stream);
 
+/*
+ * fa2_fwd_fp8 -- the forward pass of fa2_fwd with Q, K and V in FP8, both
+ * products on the FP8 matrix cores (twice the 16-bit rate): the FP8
+ * direction the infra.bea.ai FlashAttention V2 guide gives for
+ * FlashAttention-3 ("FlashAttention-3 and Beyond").
+ *
+ * q, k, v   (B, H, S, D) contiguous OCP e4m3 codes (one byte each),
+ *           16-byte aligned; element values are code * q_descale,
+ *           code * k_descale and code * v_descale.
+ * q_descale, k_descale, v_descale  finite and > 0 (FA2_ERR_SCALE).
+ * o         (B, H, S, D) contiguous, `dtype` (FA2_F16 or FA2_BF16), the
+ *           output's element type only; 16-byte aligned.
+ * lse, B, H, S, causal, scale, stream as for fa2_fwd; D is 64 or 128.
+ *
+ * Arithmetic: S = Q K^T and O~ = P V on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x
+ * e4m3, fp32 accumulation; the instruction's internal sum is not exact
+ * fp32), the online softmax in fp32, and P rounded to e4m3 as
+ * 2^(t - m + 6) (t the base-2 logit, m the running reference max, kept
+ * within 2.75 of every t so that P stays under e4m3's 448). O is divided
+ * by the sum of P as rounded and rounded once to `dtype`; lse comes from
+ * the sum of P in fp32. The result therefore differs from exact attention
+ * on the dequantized inputs by more than fa2_fwd's does: by at most a
+ * forward error bound set by the rounding of P to e4m3 (3 mantissa bits)
+ * and the FP8 product's sum, which the tests evaluate per output.
+ * Returns the codes of fa2_fwd (FA2_ERR_HEADDIM for D other than 64, 128).
+ */
+int fa2_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                int B, int H, int S, int D, int causal, float scale, float q_descale,
+                float k_descale, float v_descale, int dtype, void *stream);
+
 /* Bytes of workspace fa2_fwd_splitkv and fa2_fwd_splitkv_fp8 need for these
  * sizes and n_split; n_split = 0 gives enough for the default split count
  * of either. 0 for invalid sizes or head dims. */

@@ -17,7 +17,9 @@ What it follows (the pages' statement of the problem):
     epilogue, jared-hpc Lecture 6 reading task);
   * a KV-cache form with Sq queries against Sk keys, the queries being the
     last Sq positions (causal keeps j <= i + Sk - Sq), for the decoding
-    variant the infra.bea.ai guide names ("When V2 Is Used vs Not").
+    variant the infra.bea.ai guide names ("When V2 Is Used vs Not");
+  * beside the definition, the FP8 path's tolerance: a forward error bound
+    per output for FP8 products and P rounded to e4m3 (attn_oracle.c).
 
 Inputs are numpy fp64 arrays holding exactly the values the GPU receives.
 """
@@ -63,6 +65,9 @@ def _load():
         lib.oracle_attention_rows_f64.restype = I
         lib.oracle_attention_kv_f64.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, I, D, I]
         lib.oracle_attention_kv_f64.restype = I
+        lib.oracle_attention_fp8_bound_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, L, L, L, L,
+                                                       I, D, D, D, D, I]
+        lib.oracle_attention_fp8_bound_f64.restype = I
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -145,3 +150,28 @@ def attention_kv_f64(q, k, v, causal: bool, scale: float, nthreads: int = 0):
     if rc != 0:
         raise RuntimeError(f"oracle_attention_kv_f64 failed with code {rc}")
     return o, lse
+
+
+def attention_fp8_bound_f64(q, k, v, causal: bool, scale: float, eps_sum: float, p_exp: float,
+                            u_out: float, nthreads: int = 0):
+    """Exact attention on the given (dequantized FP8) inputs, and the
+    tolerance of the FP8 path per output: a forward error bound for
+    products whose sums are within eps_sum of exact (relative to the sum of
+    |terms|) and P rounded to e4m3 as 2^(t - m + p_exp), O rounded to an
+    output type of relative half-ulp u_out (attn_oracle.c derives it).
+
+    Returns (o, lse, bound_o, bound_lse), fp64, shaped (B,H,S,D) and (B,H,S).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, S, D = _shape4(q, k, v)
+    o = np.empty((B, H, S, D), np.float64)
+    lse = np.empty((B, H, S), np.float64)
+    bo = np.empty((B, H, S, D), np.float64)
+    bl = np.empty((B, H, S), np.float64)
+    rc = _load().oracle_attention_fp8_bound_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                _ptr(bo), _ptr(bl), B, H, S, D,
+                                                int(bool(causal)), float(scale), float(eps_sum),
+                                                float(p_exp), float(u_out), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_fp8_bound_f64 failed with code {rc}")
+    return o, lse, bo, bl

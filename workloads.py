@@ -150,6 +150,32 @@ def make_qkv_decode_fp8(w: DecodeWorkload, seed: int = 0):
     return q.to(w.torch_dtype), k8, v8
 
 
+def fp8_descales(w: Workload):
+    """Per-tensor descales of a workload's FP8 inputs: N(0, qk_mult^2) values
+    over 1/64 of that spread, so that |x| / descale stays under e4m3's 448
+    (about 5.5 standard deviations)."""
+    return w.qk_mult / 64.0, w.qk_mult / 64.0, 1.0 / 64.0
+
+
+def make_qkv_fp8(w: Workload, seed: int = 0):
+    """(q, k, v) as FP8 e4m3 codes: the fp32 draws of make_qkv (same
+    generator, order and qk_mult), each divided by its descale
+    (fp8_descales) and cast once to torch.float8_e4m3fn (round to nearest
+    even). The values they stand for are codes * descale."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    shape = (w.B, w.H, w.S, w.D)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if w.qk_mult != 1.0:
+        q = q * w.qk_mult
+        k = k * w.qk_mult
+    dq, dk, dv = fp8_descales(w)
+    f8 = torch.float8_e4m3fn
+    return tuple((x / d).clamp(-448.0, 448.0).to(f8) for x, d in ((q, dq), (k, dk), (v, dv)))
+
+
 def dequantize_fp8(codes, descale: float):
     """The values FP8 codes stand for, in fp64 (exact)."""
     return codes.to(torch.float64) * float(descale)
@@ -209,6 +235,15 @@ ALL = TINY + SWEEP + LLM_LAYER + [LONG_PREFILL, RAGGED_D256, ONE_GPU_SHARE]
 
 TOLERANCE_O = {"f16": 2e-3, "bf16": 1.6e-2}
 TOLERANCE_LSE_REL = 1e-4
+
+# Relative accuracy of the sum inside gfx950's FP8 (e4m3) matrix-core
+# product v_mfma_f32_32x32x64_f8f6f4: |result - exact| is at most this times
+# (|C_in| + sum of |products|). Not published; measured by
+# tests/test_fp8_mfma_gpu.py (worst seen 2^-12.3, on operands spanning the
+# whole e4m3 range; 2^-15 on attention-like ones; C_in itself is added
+# without loss) and held there with a 2x margin. The FP8 attention path's
+# tolerance rests on it.
+FP8_MFMA_SUM_REL = 2.0 ** -11
 
 
 def by_name(name: str) -> Workload:
