@@ -545,7 +545,28 @@ def probe():
     p.fa2_probe_mfma_ceiling.restype = i
     p.fa2_probe_mfma_flops.argtypes = [i, i]
     p.fa2_probe_mfma_flops.restype = ctypes.c_double
+    p.fa2_probe_mfma_fp8.argtypes = [vp, vp, vp, vp, i, vp]
+    p.fa2_probe_mfma_fp8.restype = i
+    p.fa2_probe_cvt_fp8.argtypes = [vp, vp, i, vp]
+    p.fa2_probe_cvt_fp8.restype = i
     return p
+
+
+def test_cvt_probe_validates_before_launch(probe):
+    A, B = 0x10000000, 0x10010000
+    assert probe.fa2_probe_cvt_fp8(None, B, 4, None) == 1
+    assert probe.fa2_probe_cvt_fp8(A, B, 6, None) == 2
+    assert probe.fa2_probe_cvt_fp8(A, B, 0, None) == 2
+    assert probe.fa2_probe_cvt_fp8(A + 4, B, 4, None) == 16
+
+
+def test_fp8_probe_validates_before_launch(probe):
+    A, B, C, D = 0x10000000, 0x10010000, 0x10020000, 0x10030000
+    assert probe.fa2_probe_mfma_fp8(None, B, C, D, 1, None) == 1
+    assert probe.fa2_probe_mfma_fp8(A, B, C, None, 1, None) == 1
+    assert probe.fa2_probe_mfma_fp8(A, B, C, D, 0, None) == 2
+    assert probe.fa2_probe_mfma_fp8(A + 16, B, C, D, 1, None) == 16
+    assert probe.fa2_probe_mfma_fp8(A, B, C + 2, D, 1, None) == 16
 
 
 def test_probe_exports_exactly_its_header(probe):
@@ -553,7 +574,8 @@ def test_probe_exports_exactly_its_header(probe):
 
     text = open(PROBE_HEADER).read()
     declared = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa2_\w+)\s*\(", text, flags=re.M)
-    assert sorted(declared) == ["fa2_probe_mfma_ceiling", "fa2_probe_mfma_flops"]
+    assert sorted(declared) == ["fa2_probe_cvt_fp8", "fa2_probe_mfma_ceiling",
+                                "fa2_probe_mfma_flops", "fa2_probe_mfma_fp8"]
     _, defined = _elf_dynamic(PROBE_LIB_PATH)
     assert sorted(n for n in defined if n.startswith("fa2")) == sorted(declared)
     for name in declared:
