@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA, MI355X
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 MFMA, MI355X (twice the 16-bit rate)
 PEAK_HBM_GBS = 8000.0
 # Timing protocol of jared-hpc Lecture 6 ("Measure it"): at least 10 warm-up
 # launches before the timed ones; the GPU clock also needs some tenths of a
@@ -82,31 +83,38 @@ def read_traffic(workload_name: str):
         return None
 
 
-def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0, balanced: bool = False):
+def time_gpu(w, steps: int, warmup: int, warmup_min_s: float = 0.0, balanced: bool = False,
+             fp8: bool = False):
     """Per-launch HIP-event durations of fa2_fwd on w (balanced: of
-    fa2_fwd_balanced, both its kernels when it splits the keys)."""
+    fa2_fwd_balanced, both its kernels when it splits the keys; fp8: of
+    fa2_fwd_fp8 on the workload's inputs as e4m3 codes, O in w's dtype)."""
     import torch
 
     import flashattention_tiled_amd as fa
     import workloads as wl
 
     dev = torch.device("cuda:0")
-    q, k, v = wl.make_qkv(w, seed=0)
+    q, k, v = (wl.make_qkv_fp8 if fp8 else wl.make_qkv)(w, seed=0)
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
-    o = torch.empty_like(qd)
+    o = torch.empty((w.B, w.H, w.S, w.D), dtype=w.torch_dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     dtype = fa.FA2_F16 if w.dtype == "f16" else fa.FA2_BF16
     lib = fa.load_library()
     args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
             w.B, w.H, w.S, w.D, int(w.causal), float(w.scale), dtype, stream.cuda_stream)
+    entry = lib.fa2_fwd
     if balanced:
         need = fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, int(w.causal))
         ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
         args = args[:9] + (None,) + args[9:12] + (ws.data_ptr(), need, stream.cuda_stream)
+        entry = lib.fa2_fwd_balanced
+    elif fp8:
+        args = args[:11] + tuple(float(d) for d in wl.fp8_descales(w)) + args[11:]
+        entry = lib.fa2_fwd_fp8
 
     def launch():
-        st = (lib.fa2_fwd_balanced if balanced else lib.fa2_fwd)(*args)
+        st = entry(*args)
         if st != 0:
             raise fa.FA2Error(st, fa.fa2_status_string(st))
 
@@ -445,10 +453,12 @@ def oracle_full_leg(w, q, k, v, o_gpu, lse_gpu, threads: int):
 
 def run_table(path: str, steps: int, warmup: int, with_oracle: bool = False):
     """Every benchmark shape through fa2_fwd (and fa2_fwd_balanced where it
-    splits the keys) into a CSV. with_oracle: also the fp64 oracle over every
-    row of each shape on all host cores (wall time, GFLOP/s, and the parity
-    of the fa2_fwd output against it), and the tiny shapes once more on one
-    thread."""
+    splits the keys, fa2_fwd_fp8 on e4m3 inputs where it has a kernel) into
+    a CSV; pct_peak is of the dense peak of the entry's input type (16-bit
+    2516.6, FP8 5033.2 TFLOP/s). with_oracle: also the fp64 oracle over every
+    row of each 16-bit shape on all host cores (wall time, GFLOP/s, and the
+    parity of the fa2_fwd output against it), and the tiny shapes once more
+    on one thread."""
     import workloads as wl
 
     import flashattention_tiled_amd as fa
@@ -456,19 +466,31 @@ def run_table(path: str, steps: int, warmup: int, with_oracle: bool = False):
     cores = len(os.sched_getaffinity(0))
     rows = []
     for w in wl.ALL:
-        # fa2_fwd, and fa2_fwd_balanced where it splits the keys of this shape
+        # fa2_fwd, fa2_fwd_balanced where it splits the keys of this shape,
+        # and fa2_fwd_fp8 (e4m3 inputs) where it has a kernel (D = 64, 128)
         entries = ["fa2_fwd"]
         if fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, int(w.causal)) > 0:
             entries.append("fa2_fwd_balanced")
+        if w.D in (64, 128) and w not in wl.TINY:
+            entries.append("fa2_fwd_fp8")
         for entry in entries:
-            r = time_gpu(w, steps, warmup, warmup_min_s=0.3, balanced=entry != "fa2_fwd")
+            fp8 = entry == "fa2_fwd_fp8"
+            r = time_gpu(w, steps, warmup, warmup_min_s=0.3, balanced=entry == "fa2_fwd_balanced",
+                         fp8=fp8)
             avg, med = stats_line(w, r)
             tf = w.flops / (med * 1e-3) / 1e12
-            gbs = w.algorithmic_bytes / (med * 1e-3) / 1e9
+            # FP8 reads 1-byte Q, K, V: its algorithmic bytes and its peak differ
+            n = w.B * w.H * w.S
+            alg = (3 * n * w.D + 2 * n * w.D + 4 * n) if fp8 else w.algorithmic_bytes
+            gbs = alg / (med * 1e-3) / 1e9
+            peak = PEAK_FP8_TFLOPS if fp8 else PEAK_TFLOPS
             line = (f"{w.name},{entry},{w.B},{w.H},{w.S},{w.D},{w.dtype},{int(w.causal)},"
                     f"{med:.4f},{avg:.4f},{min(r['durs_ms']):.4f},{tf:.1f},"
-                    f"{100 * tf / PEAK_TFLOPS:.2f},{gbs:.1f}")
-            if with_oracle:
+                    f"{100 * tf / peak:.2f},{gbs:.1f}")
+            if with_oracle and fp8:
+                rows.append(line + ",,,,,")
+                log(line)
+            elif with_oracle:
                 legs = [oracle_full_leg(w, r["q"], r["k"], r["v"], r["o"], r["lse"], cores)]
                 if w in wl.TINY:
                     legs.append(oracle_full_leg(w, r["q"], r["k"], r["v"], r["o"], r["lse"], 1))
