@@ -48,6 +48,7 @@
 using fa2_host::check_device;
 using fa2_host::extent_bytes;
 using fa2_host::overlaps;
+using fa2_host::elements_fit_int64;
 using fa2_host::rows_disjoint;
 
 namespace {
@@ -362,7 +363,7 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
 
   // K and V of this head, loaded through bounds-checked buffers that end
   // with row S - 1 (loads of rows >= S return zero).
-  const uint32_t k_bytes = (uint32_t)S * k_rb, v_bytes = (uint32_t)S * v_rb;
+  const int k_cap = rows_within_2g(k_rb), v_cap = rows_within_2g(v_rb);
   const unsigned char* k_head = (const unsigned char*)(k + k_at);
   const unsigned char* v_head = (const unsigned char*)(v + v_at);
   uint32_t k_off[LPW], v_off[LPW];
@@ -375,14 +376,8 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   }
   // buffer for key tile t of K or V (limit 0: a tile that is not needed,
   // whose loads return zero)
-  auto k_tile = [&](uint32_t limit, int t) {
-    if constexpr (STRIDED) return tile_rsrc_at(k_head, limit, (uint32_t)t * (uint32_t)Bc * k_rb);
-    else return tile_rsrc<TB>(k_head, limit, t);
-  };
-  auto v_tile = [&](uint32_t limit, int t) {
-    if constexpr (STRIDED) return tile_rsrc_at(v_head, limit, (uint32_t)t * (uint32_t)Bc * v_rb);
-    else return tile_rsrc<TB>(v_head, limit, t);
-  };
+  auto k_tile = [&](int rows, int t) { return tile_rsrc_rows(k_head, rows, t * Bc, k_rb, k_cap); };
+  auto v_tile = [&](int rows, int t) { return tile_rsrc_rows(v_head, rows, t * Bc, v_rb, v_cap); };
 
   // LDS read offsets that do not depend on the tile.
   // K^T operand: row 32 kb + l32, chunk (2 s + hi) ^ swz_k(l32).
@@ -432,18 +427,18 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   // iteration j - 1, so K of tile j + NST goes into tile j's K stage and V of
   // tile j + NST - 1 into tile j - 1's V stage. Tile t sits in stage t % NST
   // of each ring.
-  load_tile_rsrc<LPW>(k_tile(k_bytes, t0), smem + kK0, wave, k_off);
+  load_tile_rsrc<LPW>(k_tile(S, t0), smem + kK0, wave, k_off);
   if constexpr (NST == 2) {
-    load_tile_rsrc<LPW>(v_tile(v_bytes, t0), smem + kV0, wave, v_off);
-    if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(k_bytes, t0 + 1), smem + kK1, wave, k_off);
+    load_tile_rsrc<LPW>(v_tile(S, t0), smem + kV0, wave, v_off);
+    if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, t0 + 1), smem + kK1, wave, k_off);
   } else {
     // the loads iterations 1 - NST .. -1 would have issued, K then V of each
     // (a tile past the workgroup's last gets a zero-length buffer)
 #pragma unroll
     for (int i = 1; i < NST; ++i) {
-      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? k_bytes : 0u, t0 + i), smem + kK0 + i * TB, wave,
+      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, t0 + i), smem + kK0 + i * TB, wave,
                           k_off);
-      load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? v_bytes : 0u, t0 + i - 1),
+      load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? S : 0, t0 + i - 1),
                           smem + kV0 + (i - 1) * TB, wave, v_off);
     }
   }
@@ -489,8 +484,8 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     // workgroup's last gets a zero-length buffer, so its loads only write
     // zeros to a free stage
     const StepLoads<LPW> ld{
-        k_tile(j + NST < n_tiles ? k_bytes : 0u, t0 + j + NST),
-        v_tile(j + NST - 1 < n_tiles ? v_bytes : 0u, t0 + j + NST - 1),
+        k_tile(j + NST < n_tiles ? S : 0, t0 + j + NST),
+        v_tile(j + NST - 1 < n_tiles ? S : 0, t0 + j + NST - 1),
         smem + k_free, smem + v_free, k_off, v_off, wave};
     if (j < n_act) {
       // scores of tile j + 1 || probabilities of tile j, then P V of tile j
@@ -674,7 +669,9 @@ int prefill_call(const void* q, const void* k, const void* v, void* o, float* ls
                  int S, int D, const long long* strides, int causal, float scale, int dtype,
                  bool balanced, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535) return FA2_ERR_SHAPE;
+  // S leaves room for the tile indices past its end in 32-bit key counts
+  if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535 || S > INT32_MAX - 1024)
+    return FA2_ERR_SHAPE;
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
   if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
   // every stride in [0, 2^40], a multiple of 8 elements (16-byte rows), and
@@ -691,10 +688,11 @@ int prefill_call(const void* q, const void* k, const void* v, void* o, float* ls
     st = Strides{strides[0], strides[1], strides[2],  strides[3], strides[4],  strides[5],
                  strides[6], strides[7], strides[8],  strides[9], strides[10], strides[11]};
   }
-  // one head of K or V, plus a tile of rows past its end, within 32-bit byte
-  // offsets (buffer loads)
-  if (((long long)S + 256) * st.ks * 2 > (long long)INT32_MAX ||
-      ((long long)S + 256) * st.vs * 2 > (long long)INT32_MAX)
+  // the elements of every tensor within int64, and the 256 rows of K or V
+  // one tile load spans within 31-bit offsets from the tile's start (buffer
+  // loads; a head itself may span any size)
+  if (!elements_fit_int64(B, H, S, D) || 256LL * st.ks * 2 > (long long)INT32_MAX ||
+      256LL * st.vs * 2 > (long long)INT32_MAX)
     return FA2_ERR_SHAPE;
   // the kernel linearises its block index in a 32-bit int (a key split
   // only runs on grids of a few thousand workgroups)

@@ -66,9 +66,7 @@ template <int D> struct Fp8Shape {
   static_assert(kLoadsPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "wave loads");
 };
 
-// Tile max of t = c_eff * scores per row (raw scores, c_eff of either sign)
-// and whether any row of the wave exceeds its reference max by more than
-// the headroom.
+// Tile max of t = c_eff * scores per row (raw scores, c_eff of either sign).
 template <int NKB>
 __device__ __forceinline__ float fp8_tile_max(const f32x16 (&acc)[1][NKB], float c_eff) {
   float mx = -INFINITY, mn = INFINITY;
@@ -150,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
     }
   }
 
-  const uint32_t kv_bytes = (uint32_t)S * D;
+  constexpr int kv_cap = 0x7fffffff / D;  // rows one tile load may reach
   const unsigned char* k_head = k + head;
   const unsigned char* v_head = v + head;
   uint32_t k_off[LPW], v_off[LPW];
@@ -187,8 +185,8 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
   const int n_tiles = (kv_end + Bc - 1) / Bc;
   const int n_act = CAUSAL ? min(n_tiles, (wave_row0 + 32 + Bc - 1) / Bc) : n_tiles;
 
-  auto k_tile = [&](uint32_t limit, int t) { return tile_rsrc<TB>(k_head, limit, t); };
-  auto v_tile = [&](uint32_t limit, int t) { return tile_rsrc<TB>(v_head, limit, t); };
+  auto k_tile = [&](int rows, int t) { return tile_rsrc_rows(k_head, rows, t * Bc, D, kv_cap); };
+  auto v_tile = [&](int rows, int t) { return tile_rsrc_rows(v_head, rows, t * Bc, D, kv_cap); };
 
   auto scores = [&](uint32_t k_stage, f32x16 (&acc)[1][NKB]) {
 #pragma unroll
@@ -223,9 +221,9 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
   };
 
   // prologue: K and V of tile 0 and K of tile 1
-  load_tile_rsrc<LPW>(k_tile(kv_bytes, 0), smem + kK0, wave, k_off);
-  load_tile_rsrc<LPW>(v_tile(kv_bytes, 0), smem + kV0, wave, v_off);
-  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(kv_bytes, 1), smem + kK1, wave, k_off);
+  load_tile_rsrc<LPW>(k_tile(S, 0), smem + kK0, wave, k_off);
+  load_tile_rsrc<LPW>(v_tile(S, 0), smem + kV0, wave, v_off);
+  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, 1), smem + kK1, wave, k_off);
 
   f32x16 s_a[1][NKB], s_b[1][NKB];
   float ce_a[1], ce_b[1];
@@ -249,9 +247,9 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
     workgroup_barrier();
     // K of tile j + 2 into tile j's K stage, V of tile j + 1 into tile
     // j - 1's V stage (tiles past the last get zero-length buffers)
-    load_tile_rsrc<LPW>(k_tile(j + 2 < n_tiles ? kv_bytes : 0u, j + 2), smem + k_free, wave,
+    load_tile_rsrc<LPW>(k_tile(j + 2 < n_tiles ? S : 0, j + 2), smem + k_free, wave,
                         k_off);
-    load_tile_rsrc<LPW>(v_tile(j + 1 < n_tiles ? kv_bytes : 0u, j + 1), smem + v_free, wave,
+    load_tile_rsrc<LPW>(v_tile(j + 1 < n_tiles ? S : 0, j + 1), smem + v_free, wave,
                         v_off);
     if (j < n_act) {
       scores(k_next, nxt);
@@ -340,12 +338,13 @@ extern "C" int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                            int H, int S, int D, int causal, float scale, float q_descale,
                            float k_descale, float v_descale, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535) return FA2_ERR_SHAPE;
+  if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535 || S > INT32_MAX - 1024)
+    return FA2_ERR_SHAPE;
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
   if (!(D == 64 || D == 128)) return FA2_ERR_HEADDIM;
-  // one head of K or V, plus a tile past its end, within 32-bit byte offsets;
-  // the grid's linear block index in 32 bits
-  if (((long long)S + 256) * D > (long long)INT32_MAX) return FA2_ERR_SHAPE;
+  // the elements within int64 (a head may span any size: tiles are
+  // addressed from 64-bit starts); the grid's linear block index in 32 bits
+  if (!fa2_host::elements_fit_int64(B, H, S, D)) return FA2_ERR_SHAPE;
   if ((((long long)S + 127) / 128) * H * B > (long long)INT32_MAX) return FA2_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA2_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return FA2_ERR_ALIGN;

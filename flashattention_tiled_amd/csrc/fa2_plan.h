@@ -345,6 +345,18 @@ bool rows_disjoint(int B, int H, int S, int D, long long sb, long long sh, long 
   return true;
 }
 
+// Whether B * H * S * D elements (and twice that in bytes) fit in int64.
+bool elements_fit_int64(long long B, long long H, long long S, long long D) {
+  if (B < 1 || H < 1 || S < 1 || D < 1) return false;
+  const long long lim = 0x3fffffffffffffffLL;  // int64 max / 2
+  long long n = B;
+  for (long long f : {H, S, D}) {
+    if (n > lim / f) return false;
+    n *= f;
+  }
+  return true;
+}
+
 // Bytes from a strided (B, H, S, D) tensor's base pointer to the end of its
 // last element.
 size_t extent_bytes(int B, int H, int S, int D, long long sb, long long sh, long long ss,

@@ -54,8 +54,9 @@ extern "C" const char* fa2_status_string(int status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
     case FA2_ERR_SHAPE:
-      return "B, H and S must be >= 1, B and H <= 65535, one head (S*D elements) under 2 GiB, "
-             "and the grid within 2^31 workgroups";
+      return "B, H and S must be >= 1, B and H <= 65535, B*H*S*D elements (and their bytes) "
+             "within int64, the grid within 2^31 workgroups, and 256 rows of a K or V "
+             "sequence stride within 2^31 bytes";
     case FA2_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA2_ERR_DTYPE: return "dtype must be FA2_F16 or FA2_BF16";
     case FA2_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned and lse 4-byte aligned";

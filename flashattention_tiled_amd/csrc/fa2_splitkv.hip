@@ -35,6 +35,7 @@
 using fa2_host::check_device;
 using fa2_host::extent_bytes;
 using fa2_host::overlaps;
+using fa2_host::elements_fit_int64;
 using fa2_host::rows_disjoint;
 
 namespace {
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
   // K and V rows of this head, `k_rb` / `v_rb` bytes apart; buffers end
   // with key Sk - 1, so loads of keys >= Sk return zero
   const uint32_t k_rb = (uint32_t)st.ks * EB, v_rb = (uint32_t)st.vs * EB;
-  const uint32_t k_bytes = (uint32_t)Sk * k_rb, v_bytes = (uint32_t)Sk * v_rb;
+  const int k_cap = rows_within_2g(k_rb), v_cap = rows_within_2g(v_rb);
   const unsigned char* k_head = (const unsigned char*)k + (size_t)(b * st.kb + h * st.kh) * EB;
   const unsigned char* v_head = (const unsigned char*)v + (size_t)(b * st.vb + h * st.vh) * EB;
   uint32_t k_off[LPW], v_off[LPW];
@@ -237,11 +238,11 @@ __global__ __launch_bounds__(64) void fa2_splitkv_partial_kernel(
     tile_load_offsets_strided<D, LPW, true>(0, lane, v_rb, v_off);
   }
   auto load_k = [&](int t, uint32_t stage) {
-    load_tile_rsrc<LPW>(tile_rsrc_at(k_head, k_bytes, (uint32_t)t * (uint32_t)Bc * k_rb),
+    load_tile_rsrc<LPW>(tile_rsrc_rows(k_head, Sk, t * Bc, k_rb, k_cap),
                         smem + stage, 0, k_off);
   };
   auto load_v = [&](int t, uint32_t stage) {
-    load_tile_rsrc<LPW>(tile_rsrc_at(v_head, v_bytes, (uint32_t)t * (uint32_t)Bc * v_rb),
+    load_tile_rsrc<LPW>(tile_rsrc_rows(v_head, Sk, t * Bc, v_rb, v_cap),
                         smem + stage, 0, v_off);
   };
   const uint32_t k_lane = (uint32_t)(l32 * CPR * 16 + 16 * (hi ^ swz_k<D>(l32)));
@@ -443,7 +444,8 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
                  void* workspace, size_t workspace_bytes, void* stream,
                  bool use_scratch = false) {
   if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || B > 65535 || H > 65535 || n_split < 0)
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || B > 65535 || H > 65535 || n_split < 0 ||
+      Sk > INT32_MAX - 1024)
     return FA2_ERR_SHAPE;
   if (causal && Sq > Sk) return FA2_ERR_SHAPE;  // the first queries would have no key
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
@@ -464,10 +466,12 @@ int splitkv_call(const void* q, const void* k, const void* v, void* o, float* ls
       if (i % 3 == 2 && x < D) return FA2_ERR_STRIDE;
     }
   }
-  // one head of K or V, plus a tile past its end, within 32-bit byte offsets;
-  // query rows of the whole call indexed in 32 bits
-  if (((long long)Sk + 256) * st.ks * kv_elem_bytes > (long long)INT32_MAX ||
-      ((long long)Sk + 256) * st.vs * kv_elem_bytes > (long long)INT32_MAX)
+  // the elements of every tensor within int64, the 256 rows of K or V one
+  // tile load spans within 31-bit offsets from the tile's start (a head
+  // itself may span any size), query rows of the whole call indexed in 32
+  // bits
+  if (!elements_fit_int64(B, H, Sk, D) || 256LL * st.ks * kv_elem_bytes > (long long)INT32_MAX ||
+      256LL * st.vs * kv_elem_bytes > (long long)INT32_MAX)
     return FA2_ERR_SHAPE;
   if ((long long)B * H * Sq > (long long)INT32_MAX / 4) return FA2_ERR_SHAPE;
   if (strides && !rows_disjoint(B, H, Sq, D, st.ob, st.oh, st.os)) return FA2_ERR_STRIDE;

@@ -208,27 +208,28 @@ __device__ __forceinline__ void tile_load_offsets_strided(int wave, int lane, ui
   }
 }
 
-// Buffer descriptor for tile t of a head (K or V), rebased on the tile. Its
-// record count ends at `limit` bytes from the head start (the end of the
-// head, so that loads past S return zero; 0 for a tile that is not needed,
-// whose loads then all return zero).
-template <int TB>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned char* head_base,
-                                                            uint32_t limit, int t) {
-  // both values are wave-uniform; readfirstlane keeps them (and so the buffer
-  // descriptor) in scalar registers
-  const uint32_t start = (uint32_t)t * TB;
-  const uint32_t left = (uint32_t)wave_uniform((int)(limit - (start < limit ? start : limit)));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + start), 0, (int)left, kBufferFlags);
+// Buffer descriptor for the K or V rows from row0 on of a head whose rows
+// are row_bytes apart, based at row row0. Its record count covers the rows
+// left before `rows` (the end of the head, so that loads past it return
+// zero; 0 for a tile that is not needed, whose loads then all return zero),
+// at most cap_rows of them, where cap_rows * row_bytes < 2^31: the rows one
+// tile load reaches through its 32-bit offsets. The base is a 64-bit
+// address, so a head may span any size; the count stays in 32-bit
+// arithmetic. All values are wave-uniform; readfirstlane keeps them (and so
+// the descriptor) in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc_rows(const unsigned char* head_base,
+                                                                 int rows, int row0,
+                                                                 uint32_t row_bytes, int cap_rows) {
+  const int r0 = wave_uniform(row0);
+  const int left = wave_uniform(min(max(rows - r0, 0), cap_rows));
+  return __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(head_base + (uint64_t)(uint32_t)r0 * row_bytes), 0,
+      (int)((uint32_t)left * row_bytes), kBufferFlags);
 }
 
-// The same for a tile that starts `start` bytes after the head start (a
-// strided K or V, whose tiles are B_c rows x the row stride apart).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc_at(const unsigned char* head_base,
-                                                               uint32_t limit, uint32_t start) {
-  const uint32_t s0 = (uint32_t)wave_uniform((int)start);
-  const uint32_t left = (uint32_t)wave_uniform((int)(limit - (s0 < limit ? s0 : limit)));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(head_base + s0), 0, (int)left, kBufferFlags);
+// The largest cap_rows of tile_rsrc_rows for rows row_bytes apart.
+__device__ __forceinline__ int rows_within_2g(uint32_t row_bytes) {
+  return (int)(0x7fffffffu / row_bytes);
 }
 
 // Block i (of this wave's LPW) of a tile load into LDS at `dst`: 64 lanes x
@@ -238,16 +239,6 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t rsrc, unsigned
                                            int wave, uint32_t off, int i) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * LPW + i) * 1024), 16,
                                            off, 0, 0, 0);
-}
-
-// Start loading a whole tile (this wave's LPW blocks).
-template <int LPW, int TB>
-__device__ __forceinline__ void load_tile(const unsigned char* head_base, uint32_t head_bytes,
-                                          int t, unsigned char* dst, int wave,
-                                          const uint32_t* off) {
-  const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc<TB>(head_base, head_bytes, t);
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) load_block<LPW>(rsrc, dst, wave, off[i], i);
 }
 
 // Start loading a whole tile (this wave's LPW blocks) through `rsrc`.

@@ -45,7 +45,9 @@ typedef enum {
 typedef enum {
     FA2_OK = 0,
     FA2_ERR_NULL = 1,      /* a tensor pointer is NULL */
-    FA2_ERR_SHAPE = 2,     /* B, H or S < 1, H or B > 65535, or B*H*S*D overflows int64 */
+    FA2_ERR_SHAPE = 2,     /* B, H or S < 1, H or B > 65535, B*H*S*D elements (or their
+                              bytes) overflow int64, the grid passes 2^31 workgroups, or
+                              (strided) 256 rows of K or V span 2^31 bytes or more */
     FA2_ERR_HEADDIM = 3,   /* D is not 64, 128 or 256 */
     FA2_ERR_DTYPE = 4,     /* dtype is not FA2_F16 or FA2_BF16 */
     FA2_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
@@ -113,8 +115,9 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  *          (a K/V shared by all heads), but o's rows must be disjoint.
  * lse      contiguous (B, H, S) floats, as for fa2_fwd.
  * Other arguments, the result and the arithmetic are those of fa2_fwd, and
- * for contiguous strides the result is bit-identical to it. One head of K
- * and of V must span under 2 GiB: (S + 256) * sequence stride * 2 bytes.
+ * for contiguous strides the result is bit-identical to it. A head may
+ * span any size, but 256 rows of K and of V must span under 2^31 bytes
+ * (256 * sequence stride * 2), the reach of one tile load's offsets.
  * Overlap is judged on the byte range each tensor spans, so o and lse must
  * not fall within q's, k's or v's span. Returns FA2_ERR_STRIDE for bad
  * strides, otherwise the codes of fa2_fwd.
@@ -265,8 +268,9 @@ int fa2_fwd_splitkv_fp8(const void *q, const void *k, const void *v, void *o, fl
  *          for 16-bit tensors, of 16 for FP8 K and V); each sequence stride
  *          is >= D; o's rows must be disjoint. K and V may repeat one head
  *          (head stride 0).
- * lse      contiguous (B, H, Sq) floats. One head of K and of V must span
- *          under 2 GiB: (Sk + 256) * sequence stride * element bytes.
+ * lse      contiguous (B, H, Sq) floats. 256 rows of K and of V must span
+ *          under 2^31 bytes (256 * sequence stride * element bytes); a head
+ *          may span any size.
  * The workspace, the other arguments and the result are those of the
  * contiguous calls, which the strided call reproduces bit for bit.
  * FA2_ERR_STRIDE for bad strides, FA2_ERR_DTYPE for kv_fp8 other than 0 or

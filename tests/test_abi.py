@@ -189,6 +189,28 @@ def test_no_device_status_without_gpu(lib):
     assert _call() == fa.FA2_ERR_NO_DEVICE
 
 
+def test_heads_past_2gib_are_valid(lib):
+    """A head of K and V may span more than 2 GiB (tiles are addressed from
+    64-bit starts): S = 2000 rows 2^20 elements apart (4 GiB) get as far as
+    the device lookup, and so does a decode against 2^23 + 5 keys; an
+    element count past int64 is refused."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the fake pointers must not be launched on")
+    S, D = 2000, 64
+    far = [x << 40 for x in range(1, 6)]  # q, k, v, o, lse far apart
+    st = [S * D, S * D, D, S << 20, S << 20, 1 << 20, S << 20, S << 20, 1 << 20,
+          S * D, S * D, D]
+    assert fa.fa2_fwd_strided(far[0], far[1], far[2], far[3], far[4], 1, 1, S, D, st, 1, 0.125,
+                              fa.FA2_F16, None) == fa.FA2_ERR_NO_DEVICE
+    ws = fa.fa2_splitkv_workspace_bytes(1, 1, 3, (1 << 23) + 5, 128, 4)
+    assert fa.fa2_fwd_splitkv(far[0], far[1], far[2], far[3], far[4], 1, 1, 3, (1 << 23) + 5,
+                              128, 1, 0.125, fa.FA2_F16, 4, 6 << 40, ws,
+                              None) == fa.FA2_ERR_NO_DEVICE
+    assert fa.fa2_fwd(far[0], far[1], far[2], far[3], far[4], 65535, 65535, 2**31 - 1, 256, 0,
+                      0.125, fa.FA2_F16, None) == fa.FA2_ERR_SHAPE
+
+
 @pytest.mark.parametrize("scale", [-0.125, -1.0 / 64 ** 0.5, -0.0, -1e30])
 def test_negative_scale_is_valid(lib, scale):
     """Any finite scale passes validation, negative ones included: the
@@ -240,7 +262,7 @@ _STRIDED_CASES = [
     (dict(strides=_with(_CONTIG, s10=64)), fa.FA2_ERR_STRIDE),         # o heads share rows
     (dict(strides=_with(_CONTIG, s9=0)), fa.FA2_ERR_STRIDE),           # o batch broadcast
     (dict(strides=_with(_CONTIG, s11=64 + 8, s10=100 * 64)), fa.FA2_ERR_STRIDE),  # rows spill into next head
-    (dict(strides=_with(_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),      # a K head past 2 GiB
+    (dict(strides=_with(_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),      # 256 K rows span 2^32 B
     (dict(k=SK + 8), fa.FA2_ERR_ALIGN),
     (dict(lse=SL + 2), fa.FA2_ERR_ALIGN),
     (dict(scale=float("inf")), fa.FA2_ERR_SCALE),
@@ -360,7 +382,7 @@ def test_splitkv_workspace_bytes(lib):
     (dict(n_split=-1), fa.FA2_ERR_SHAPE),
     (dict(n_split=70000, workspace_bytes=1 << 40), fa.FA2_ERR_SHAPE),
     (dict(causal=1, Sq=_SK + 1), fa.FA2_ERR_SHAPE),
-    (dict(Sk=2**31 - 1), fa.FA2_ERR_SHAPE),
+    (dict(B=65535, H=65535, Sk=2**31 - 1), fa.FA2_ERR_SHAPE),  # elements past int64
     (dict(D=96), fa.FA2_ERR_HEADDIM),
     (dict(dtype=3), fa.FA2_ERR_DTYPE),
     (dict(k=KS + 8), fa.FA2_ERR_ALIGN),
@@ -474,7 +496,7 @@ def _call_splitkv_strided(**kw):
     (dict(strides=_with(_SKV_CONTIG, s5=72), kv_fp8=1, k_descale=0.1,
           v_descale=0.1), fa.FA2_ERR_STRIDE),                            # FP8 rows of 72 bytes
     (dict(strides=_with(_SKV_CONTIG, s10=0, s9=0), H=2, B=2), fa.FA2_ERR_STRIDE),  # o rows shared
-    (dict(strides=_with(_SKV_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),   # a K head past 2 GiB
+    (dict(strides=_with(_SKV_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),   # 256 K rows span 2^32 B
     (dict(kv_fp8=1, k_descale=0.0), fa.FA2_ERR_SCALE),
     (dict(o=KS + 64), fa.FA2_ERR_ALIAS),
 ])
