@@ -66,21 +66,17 @@ template <int D> struct Fp8Shape {
   static_assert(kLoadsPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "wave loads");
 };
 
-// Tile max of t = c_eff * scores per row (raw scores, c_eff of either sign).
+// Tile max of t = c_eff * scores per row. c_eff is never negative here: the
+// kernel takes a negative scale as its magnitude with Q's codes negated
+// (masked tiles are scaled already, c_eff = 1).
 template <int NKB>
 __device__ __forceinline__ float fp8_tile_max(const f32x16 (&acc)[1][NKB], float c_eff) {
-  float mx = -INFINITY, mn = INFINITY;
+  float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      mx = fmaxf(fmaxf(mx, acc[0][kb][r]), acc[0][kb][r + 1]);
-      mn = fminf(fminf(mn, acc[0][kb][r]), acc[0][kb][r + 1]);
-    }
-  // masked entries are -inf already scaled (c_eff = 1), so the max is the
-  // one that counts; an all -inf half gives -inf from either side
-  const float t = c_eff >= 0.f ? mx * c_eff : mn * c_eff;
-  return xor32_max(t);
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, acc[0][kb][r]), acc[0][kb][r + 1]);
+  return xor32_max(mx * c_eff);
 }
 
 // P8 of one tile for this lane's row: 32 values 2^(t - m + kP8Exp), their
@@ -137,14 +133,18 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
   const int wave_row0 = q0 + wave * 32;
   const size_t head = (size_t)bh * (size_t)S * D;
 
-  // Q^T operands: k-step s of this lane's row, dims 64 s + 32 hi .. + 31
+  // Q^T operands: k-step s of this lane's row, dims 64 s + 32 hi .. + 31.
+  // A negative scale is taken as its magnitude with every Q code negated
+  // (the sign bit flipped: exact), so the score scale c is never negative.
+  const int q_sign = c < 0.f ? (int)0x80808080 : 0;
+  c = fabsf(c);
   i32x8 qf[NKS];
   {
     const int row = wave_row0 + l32;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       qf[s] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < S) qf[s] = *(const i32x8*)(q + head + (size_t)row * D + 64 * s + 32 * hi);
+      if (row < S) qf[s] = *(const i32x8*)(q + head + (size_t)row * D + 64 * s + 32 * hi) ^ q_sign;
     }
   }
 
