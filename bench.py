@@ -12,6 +12,7 @@ Prints one JSON line on stdout; diagnostics go to stderr.
     python bench.py --decode-table PATH   # split-KV decode shapes, GB/s
     python bench.py --layer           # attention layer it/s and peak memory
     python bench.py --mfma-ceiling    # matrix-core rate and clock on random fp16 data
+    python bench.py --fp8 [--workload NAME]   # the FP8 prefill, against the FP8 peak
 
 Metric: TFLOP/s with FLOPs = 4*B*H*S^2*D, halved for causal masking, and the
 fraction of the MI355X dense fp16/bf16 matrix-core peak (256 CUs x 2.4 GHz x
@@ -509,6 +510,32 @@ def run_table(path: str, steps: int, warmup: int, with_oracle: bool = False):
         f.write("\n".join(rows) + "\n")
 
 
+def run_fp8(w, args):
+    """The FP8 prefill (fa2_fwd_fp8) on w's inputs as e4m3 codes (workloads.make_qkv_fp8),
+    O in w's dtype: one JSON line with its TFLOP/s under the benchmark's FLOP
+    count and its fraction of the dense FP8 peak. A reduced-precision
+    variant: never the headline metric, which is the 16-bit path's."""
+    r = time_gpu(w, args.steps, max(args.warmup, WARMUP_MIN_LAUNCHES), warmup_min_s=WARMUP_MIN_S,
+                 fp8=True)
+    avg, med = stats_line(w, r)
+    ms_per_step = 1e3 * r["wall_s"] / args.steps
+    log(f"[bench] fp8 kernel avg {avg:.4f} ms, median {med:.4f} ms, min {r['durs_ms'][0]:.4f} ms, "
+        f"max {r['durs_ms'][-1]:.4f} ms; wall {ms_per_step:.4f} ms/step")
+    achieved = w.flops / (avg * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "FP8 (e4m3 Q, K, V) attention fwd TFLOP/s and % of FP8 MFMA peak",
+        "value": round(w.flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
+                   "causal": w.causal, "out_dtype": w.dtype, "flops_per_step": w.flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "kernel_ms_avg": round(avg, 5), "kernel_ms_median": round(med, 5)},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -525,6 +552,9 @@ def main():
                     help="time the attention layer against a score-materialising layer")
     ap.add_argument("--decode-table", default=None,
                     help="time the split-KV path on every decode shape into a CSV")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 (e4m3 Q, K, V) prefill on --workload instead: one JSON "
+                         "line against the 5.0 PFLOP/s FP8 peak (not the headline metric)")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only run the matrix-core ceiling probe and print its rate and clock")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -573,6 +603,9 @@ def main():
         return
 
     w = wl.by_name(args.workload)
+    if args.fp8:
+        run_fp8(w, args)
+        return
     log(f"[bench] {w} steps={args.steps} warmup={args.warmup}")
     # warm-up: the requested launches, at least WARMUP_MIN_LAUNCHES of them,
     # then more until WARMUP_MIN_S of launches have run, so that the timed

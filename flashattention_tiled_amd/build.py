@@ -57,15 +57,28 @@ def build_probe(force: bool = True) -> str:
     return PROBE_LIB_PATH
 
 
-def prefill_kernel_sha() -> str:
-    """SHA-256 over the prefill kernel's source files (name and bytes of each),
-    which keys measurements taken of that kernel to the code they measured."""
+# the files that hold the split-KV kernels' code (partial and combine)
+SPLITKV_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
+                          ("fa2_plan.h", "fa2_tile.h", "fa2_combine.h", "fa2_splitkv.hip")]
+# the files that hold the FP8 prefill kernel's code
+FP8_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
+                      ("fa2_plan.h", "fa2_tile.h", "fa2_fwd.hip", "fa2_fwd_fp8.hip")]
+
+
+def sources_sha(paths) -> str:
+    """SHA-256 over source files (name and bytes of each), which keys
+    measurements taken of a kernel to the code they measured."""
     h = hashlib.sha256()
-    for path in PREFILL_KERNEL_SOURCES:
+    for path in paths:
         h.update(os.path.basename(path).encode() + b"\0")
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def prefill_kernel_sha() -> str:
+    """SHA-256 over the prefill kernel's source files (sources_sha)."""
+    return sources_sha(PREFILL_KERNEL_SOURCES)
 
 
 if __name__ == "__main__":
