@@ -271,6 +271,110 @@ __device__ __forceinline__ void pipeline_block(
   }
 }
 
+// One step of the unpipelined loop on tile j (kPipelined = 0): its scores
+// on the matrix cores, with this wave's share of the loads of tile
+// j + NST - 1 issued between them; the mask; on the wave's first tile the
+// reference max; P and the lazy-rescale test (and, rarely, the redo); then
+// the P V product. One score buffer instead of two; the SIMD's other waves
+// fill the gaps this leaves on the matrix cores and the vector unit.
+template <int D, int DT, int RB, int NKB, int LPW, int LEVERY, bool CAUSAL>
+__device__ __forceinline__ void serial_block(
+    const StepLoads<LPW>& ld, const unsigned char* smem, uint32_t k_stage, uint32_t v_stage,
+    uint32_t k_lane, uint32_t vt_x, const u32x4 (&qf)[RB][D / 16], int key0, int row0, int S,
+    float c, int l32, int hi, bool first, float (&m_run)[RB], float (&l_run)[RB],
+    float (&l_rnd)[RB], f32x16 (&acc_o)[RB][D / 32]) {
+  using E = Elem<DT>;
+  constexpr int CPR = D / 8, NDS = D / 16, NDB = D / 32;
+  constexpr int NS1 = NKB * NDS;       // score k-steps
+  constexpr int NS2 = NKB * 2 * NDB;   // P V steps
+  constexpr int PFK = 2, PFV = 2;      // operand read-ahead (steps)
+  static_assert(LEVERY == 0 || (NS1 + LEVERY - 1) / LEVERY >= 2 * LPW,
+                "the load spacing must leave a k-step for every load block");
+
+  f32x16 sc[RB][NKB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sc[rb][kb] = f32x16{};
+  const uint32_t k_base = k_stage + k_lane;
+  auto k_read = [&](int st) {
+    const int kb = st / NDS, s = st % NDS;
+    const uint32_t off = (k_base ^ (uint32_t)(32 * s)) + (uint32_t)(kb * 32 * CPR * 16);
+    return *(const u32x4*)(smem + off);
+  };
+  u32x4 kq[PFK];
+#pragma unroll
+  for (int i = 0; i < PFK; ++i)
+    if (i < NS1) kq[i] = k_read(i);
+#pragma unroll
+  for (int st = 0; st < NS1; ++st) {
+    const int kb = st / NDS, s = st % NDS;
+    if (LEVERY == 0) {
+      if (st == 0)
+#pragma unroll
+        for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
+    } else if (st % LEVERY == 0 && st / LEVERY < 2 * LPW) {
+      ld.issue(st / LEVERY);
+      __builtin_amdgcn_sched_barrier(0x786);
+    }
+    const u32x4 a = kq[st % PFK];
+    if (st + PFK < NS1) kq[st % PFK] = k_read(st + PFK);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sc[rb][kb] = E::mfma(a, qf[rb][s], sc[rb][kb]);
+  }
+
+  float ce[RB];
+  if (tile_needs_mask<RB, NKB, CAUSAL>(key0, row0, S)) {
+    tile_mask<RB, NKB, CAUSAL>(sc, key0, row0, S, c, l32, hi, ce);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) ce[rb] = c;
+  }
+  // the first tile holds an unmasked key for every row (its first key is at
+  // most the tile's first row), so m is finite from here on
+  if (first) tile_max<RB, NKB>(sc, ce, m_run);
+  const unsigned char* v_lds = smem + v_stage;
+  auto v_read = [&](int st) {
+    const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
+    const unsigned char* vp = v_lds + (32 * kb + 16 * h) * CPR * 16 + (vt_x ^ (uint32_t)(64 * db));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vp);
+    const s16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * CPR * 16));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+    return u32x4{lo2[0], lo2[1], up2[0], up2[1]};
+  };
+  float tsum[RB], trnd[RB];
+  u32x4 pb[RB][NKB][2];
+  tile_probs<DT, RB, NKB>(sc, ce, m_run, tsum, trnd, pb);
+  bool big = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) big |= !(tsum[rb] <= kSumLimit);
+  if (__builtin_amdgcn_ballot_w64(big) != 0) {
+    // rows whose m does not move recompute the same P
+    float tm[RB];
+    tile_max<RB, NKB>(sc, ce, tm);
+    raise_max<RB, NDB>(tm, m_run, l_run, l_rnd, acc_o);
+    tile_probs<DT, RB, NKB>(sc, ce, m_run, tsum, trnd, pb);
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    l_run[rb] += tsum[rb];
+    l_rnd[rb] += trnd[rb];
+  }
+
+  u32x4 vq[PFV];
+#pragma unroll
+  for (int i = 0; i < PFV; ++i)
+    if (i < NS2) vq[i] = v_read(i);
+#pragma unroll
+  for (int st = 0; st < NS2; ++st) {
+    const int kb = st / (2 * NDB), h = (st / NDB) % 2, db = st % NDB;
+    const u32x4 a = vq[st % PFV];
+    if (st + PFV < NS2) vq[st % PFV] = v_read(st + PFV);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc_o[rb][db] = E::mfma(a, pb[rb][kb][h], acc_o[rb][db]);
+  }
+}
+
 // Element strides of the batch, head and sequence dims of Q, K, V and O (the
 // head dim is contiguous). Read only by the STRIDED kernels; the others use
 // the contiguous (B, H, S, D) layout.
@@ -427,109 +531,150 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   // iteration j - 1, so K of tile j + NST goes into tile j's K stage and V of
   // tile j + NST - 1 into tile j - 1's V stage. Tile t sits in stage t % NST
   // of each ring.
-  load_tile_rsrc<LPW>(k_tile(S, t0), smem + kK0, wave, k_off);
-  if constexpr (NST == 2) {
-    load_tile_rsrc<LPW>(v_tile(S, t0), smem + kV0, wave, v_off);
-    if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, t0 + 1), smem + kK1, wave, k_off);
+  if constexpr (!SH::kPipelined) {
+    // Unpipelined: iteration j computes tile j from stage j % NST, after
+    // every load of iteration j - NST + 1 (tile j) has landed and every wave
+    // is done with iteration j - 1, whose stage then takes tile j + NST - 1.
+#pragma unroll
+    for (int i = 0; i + 1 < NST; ++i) {
+      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, t0 + i), smem + kK0 + i * TB, wave, k_off);
+      load_tile_rsrc<LPW>(v_tile(i < n_tiles ? S : 0, t0 + i), smem + kV0 + i * TB, wave, v_off);
+    }
+    auto step_s = [&](auto sj_c, int j) {
+      constexpr int SJ = decltype(sj_c)::value, SF = (SJ + NST - 1) % NST;
+      wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
+      workgroup_barrier();
+      const int tn = j + NST - 1;
+      const StepLoads<LPW> ld{k_tile(tn < n_tiles ? S : 0, t0 + tn),
+                              v_tile(tn < n_tiles ? S : 0, t0 + tn),
+                              smem + kK0 + SF * TB, smem + kV0 + SF * TB, k_off, v_off, wave};
+      if (j < n_act) {
+        serial_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery, CAUSAL>(
+            ld, smem, kK0 + SJ * TB, kV0 + SJ * TB, k_lane, vt_x, qf, (t0 + j) * Bc, wave_row0,
+            S, c, l32, hi, j == 0, m_run, l_run, l_rnd, acc_o);
+      } else {
+#pragma unroll
+        for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
+      }
+    };
+    auto step_su = [&](auto u, int j0) {
+      constexpr int UU = decltype(u)::value;
+      if constexpr (UU < NST)
+        if (UU == 0 || j0 + UU < n_tiles) step_s(std::integral_constant<int, UU>{}, j0 + UU);
+    };
+    for (int j = 0; j < n_tiles; j += NST) {
+      step_su(std::integral_constant<int, 0>{}, j);
+      step_su(std::integral_constant<int, 1>{}, j);
+      step_su(std::integral_constant<int, 2>{}, j);
+      step_su(std::integral_constant<int, 3>{}, j);
+    }
+    static_assert(NST <= 4, "unroll");
   } else {
-    // the loads iterations 1 - NST .. -1 would have issued, K then V of each
-    // (a tile past the workgroup's last gets a zero-length buffer)
-#pragma unroll
-    for (int i = 1; i < NST; ++i) {
-      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, t0 + i), smem + kK0 + i * TB, wave,
-                          k_off);
-      load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? S : 0, t0 + i - 1),
-                          smem + kV0 + (i - 1) * TB, wave, v_off);
-    }
-  }
-
-  f32x16 s_a[RB][NKB], s_b[RB][NKB];
-  float ce_a[RB], ce_b[RB];
-  // all of them (and the Q loads, which the compiler may have issued after
-  // them) before the first tile's scores
-  wait_vm_lgkm0<0>();
-  workgroup_barrier();
-  if (n_act > 0) {
-    // m starts at the row max of tile t0, which holds an unmasked key for
-    // every row (key t0 B_c <= q0), so m is finite from here on
-    tile_scores<D, DT, RB, NKB>(smem, kK0, k_lane, qf, s_a);
-    tile_mask<RB, NKB, CAUSAL>(s_a, t0 * Bc, wave_row0, S, c, l32, hi, ce_a);
-    tile_max<RB, NKB>(s_a, ce_a, m_run);
-  }
-
-  // One pipeline step for tile j with parity PAR = j % 2 and ring stage
-  // SJ = j % NST (both known at compile time: the loop is unrolled by a
-  // multiple of 2 and of NST); `cur` holds tile j's scores, `nxt` receives
-  // tile j + 1's.
-  auto step = [&](auto par, auto sj_c, int j, f32x16 (&cur)[RB][NKB], float (&ce_cur)[RB],
-                  f32x16 (&nxt)[RB][NKB], float (&ce_nxt)[RB]) {
-    constexpr int PAR = decltype(par)::value, SJ = decltype(sj_c)::value;
-    uint32_t k_next, k_free, v_cur, v_free;  // K of tile j + 1, of tile j (done);
-                                             // V of tile j, of tile j - 1 (done)
+    load_tile_rsrc<LPW>(k_tile(S, t0), smem + kK0, wave, k_off);
     if constexpr (NST == 2) {
-      k_next = PAR ? kK0 : kK1;
-      k_free = PAR ? kK1 : kK0;
-      v_cur = PAR ? kV1 : kV0;
-      v_free = PAR ? kV0 : kV1;
+      load_tile_rsrc<LPW>(v_tile(S, t0), smem + kV0, wave, v_off);
+      if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, t0 + 1), smem + kK1, wave, k_off);
     } else {
-      constexpr int sn = (SJ + 1) % NST, sp = (SJ + NST - 1) % NST;
-      k_next = kK0 + (uint32_t)(sn * TB);
-      k_free = kK0 + (uint32_t)(SJ * TB);
-      v_cur = kV0 + (uint32_t)(SJ * TB);
-      v_free = kV0 + (uint32_t)(sp * TB);
-    }
-    wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
-    workgroup_barrier();
-    // K of tile j + NST and V of tile j + NST - 1; a tile past the
-    // workgroup's last gets a zero-length buffer, so its loads only write
-    // zeros to a free stage
-    const StepLoads<LPW> ld{
-        k_tile(j + NST < n_tiles ? S : 0, t0 + j + NST),
-        v_tile(j + NST - 1 < n_tiles ? S : 0, t0 + j + NST - 1),
-        smem + k_free, smem + v_free, k_off, v_off, wave};
-    if (j < n_act) {
-      // scores of tile j + 1 || probabilities of tile j, then P V of tile j
-      // (past the wave's last tile the scores come from a stale stage and are
-      // never used)
-      pipeline_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery>(
-          ld, smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt, acc_o);
-      if (j + 1 < n_act) {
-        if (tile_needs_mask<RB, NKB, CAUSAL>((t0 + j + 1) * Bc, wave_row0, S)) {
-          tile_mask<RB, NKB, CAUSAL>(nxt, (t0 + j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
-        } else {
+      // the loads iterations 1 - NST .. -1 would have issued, K then V of each
+      // (a tile past the workgroup's last gets a zero-length buffer)
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) ce_nxt[rb] = c;
+      for (int i = 1; i < NST; ++i) {
+        load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, t0 + i), smem + kK0 + i * TB, wave,
+                            k_off);
+        load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? S : 0, t0 + i - 1),
+                            smem + kV0 + (i - 1) * TB, wave, v_off);
+      }
+    }
+
+    f32x16 s_a[RB][NKB], s_b[RB][NKB];
+    float ce_a[RB], ce_b[RB];
+    // all of them (and the Q loads, which the compiler may have issued after
+    // them) before the first tile's scores
+    wait_vm_lgkm0<0>();
+    workgroup_barrier();
+    if (n_act > 0) {
+      // m starts at the row max of tile t0, which holds an unmasked key for
+      // every row (key t0 B_c <= q0), so m is finite from here on
+      tile_scores<D, DT, RB, NKB>(smem, kK0, k_lane, qf, s_a);
+      tile_mask<RB, NKB, CAUSAL>(s_a, t0 * Bc, wave_row0, S, c, l32, hi, ce_a);
+      tile_max<RB, NKB>(s_a, ce_a, m_run);
+    }
+
+    // One pipeline step for tile j with parity PAR = j % 2 and ring stage
+    // SJ = j % NST (both known at compile time: the loop is unrolled by a
+    // multiple of 2 and of NST); `cur` holds tile j's scores, `nxt` receives
+    // tile j + 1's.
+    auto step = [&](auto par, auto sj_c, int j, f32x16 (&cur)[RB][NKB], float (&ce_cur)[RB],
+                    f32x16 (&nxt)[RB][NKB], float (&ce_nxt)[RB]) {
+      constexpr int PAR = decltype(par)::value, SJ = decltype(sj_c)::value;
+      uint32_t k_next, k_free, v_cur, v_free;  // K of tile j + 1, of tile j (done);
+                                               // V of tile j, of tile j - 1 (done)
+      if constexpr (NST == 2) {
+        k_next = PAR ? kK0 : kK1;
+        k_free = PAR ? kK1 : kK0;
+        v_cur = PAR ? kV1 : kV0;
+        v_free = PAR ? kV0 : kV1;
+      } else {
+        constexpr int sn = (SJ + 1) % NST, sp = (SJ + NST - 1) % NST;
+        k_next = kK0 + (uint32_t)(sn * TB);
+        k_free = kK0 + (uint32_t)(SJ * TB);
+        v_cur = kV0 + (uint32_t)(SJ * TB);
+        v_free = kV0 + (uint32_t)(sp * TB);
+      }
+      wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
+      workgroup_barrier();
+      // K of tile j + NST and V of tile j + NST - 1; a tile past the
+      // workgroup's last gets a zero-length buffer, so its loads only write
+      // zeros to a free stage
+      const StepLoads<LPW> ld{
+          k_tile(j + NST < n_tiles ? S : 0, t0 + j + NST),
+          v_tile(j + NST - 1 < n_tiles ? S : 0, t0 + j + NST - 1),
+          smem + k_free, smem + v_free, k_off, v_off, wave};
+      if (j < n_act) {
+        // scores of tile j + 1 || probabilities of tile j, then P V of tile j
+        // (past the wave's last tile the scores come from a stale stage and are
+        // never used)
+        pipeline_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery>(
+            ld, smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt,
+            acc_o);
+        if (j + 1 < n_act) {
+          if (tile_needs_mask<RB, NKB, CAUSAL>((t0 + j + 1) * Bc, wave_row0, S)) {
+            tile_mask<RB, NKB, CAUSAL>(nxt, (t0 + j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
+          } else {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) ce_nxt[rb] = c;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
+      }
+    };
+    // unrolled by U steps, a multiple of 2 (score buffers) and of NST (stages)
+    constexpr int U = NST % 2 == 0 ? NST : 2 * NST;
+    auto step_u = [&](auto u, int j0) {
+      constexpr int UU = decltype(u)::value;
+      if constexpr (UU < U) {
+        if (UU == 0 || j0 + UU < n_tiles) {
+          if constexpr (UU % 2 == 0)
+            step(std::integral_constant<int, 0>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
+                 s_a, ce_a, s_b, ce_b);
+          else
+            step(std::integral_constant<int, 1>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
+                 s_b, ce_b, s_a, ce_a);
         }
       }
-    } else {
-#pragma unroll
-      for (int n = 0; n < 2 * LPW; ++n) ld.issue(n);
+    };
+    for (int j = 0; j < n_tiles; j += U) {
+      step_u(std::integral_constant<int, 0>{}, j);
+      step_u(std::integral_constant<int, 1>{}, j);
+      step_u(std::integral_constant<int, 2>{}, j);
+      step_u(std::integral_constant<int, 3>{}, j);
+      step_u(std::integral_constant<int, 4>{}, j);
+      step_u(std::integral_constant<int, 5>{}, j);
     }
-  };
-  // unrolled by U steps, a multiple of 2 (score buffers) and of NST (stages)
-  constexpr int U = NST % 2 == 0 ? NST : 2 * NST;
-  auto step_u = [&](auto u, int j0) {
-    constexpr int UU = decltype(u)::value;
-    if constexpr (UU < U) {
-      if (UU == 0 || j0 + UU < n_tiles) {
-        if constexpr (UU % 2 == 0)
-          step(std::integral_constant<int, 0>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
-               s_a, ce_a, s_b, ce_b);
-        else
-          step(std::integral_constant<int, 1>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
-               s_b, ce_b, s_a, ce_a);
-      }
-    }
-  };
-  for (int j = 0; j < n_tiles; j += U) {
-    step_u(std::integral_constant<int, 0>{}, j);
-    step_u(std::integral_constant<int, 1>{}, j);
-    step_u(std::integral_constant<int, 2>{}, j);
-    step_u(std::integral_constant<int, 3>{}, j);
-    step_u(std::integral_constant<int, 4>{}, j);
-    step_u(std::integral_constant<int, 5>{}, j);
+    static_assert(U <= 6, "unroll");
   }
-  static_assert(U <= 6, "unroll");
   // the last steps' loads (zeros into free stages) must land before the
   // workgroup's LDS is released
   wait_vm_lgkm0<0>();

@@ -27,21 +27,27 @@ namespace {
 //   kLoadEvery     phase-1 k-steps between this wave's tile-load blocks (0: all
 //                  at the start of the step)
 //   kStages        stages of the K ring and of the V ring (default 2)
-// Iteration j reads K of tile j + 1 and V of tile j while K of tile
-// j + kStages and V of tile j + kStages - 1 load, so a tile's loads have
-// kStages - 1 iterations to land. Two stages fit two workgroups per compute
-// unit at D <= 128. D = 256 holds one workgroup per unit (its registers allow
-// one wave per SIMD) and spends its LDS on 64-key tiles (2 x 2 x 32 KiB);
-// with 32-key tiles, four stages were best.
+//   kPipelined     1: a wave computes tile j + 1's scores beside tile j's
+//                  softmax (two score buffers); 0: scores, softmax and P V of
+//                  tile j in sequence, one score buffer, and the other waves
+//                  of the SIMD fill the gaps (for registers too tight for two)
+// Pipelined, iteration j reads K of tile j + 1 and V of tile j while K of
+// tile j + kStages and V of tile j + kStages - 1 load; unpipelined, it reads
+// K and V of tile j while those of tile j + kStages - 1 load. Either way a
+// tile's loads have kStages - 1 iterations to land. Two stages fit two workgroups per compute
+// unit at D <= 128. At D = 256 two score buffers leave registers for one wave
+// per SIMD only; one buffer (the unpipelined loop) fits two, and two
+// workgroups of 32-key tiles with two stages (2 x 2 x 16 KiB each) share a
+// unit's LDS.
 // The defaults are the best of a sweep over these values on the benchmark
 // shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides one, as
-// "waves, row blocks, keys, waves per SIMD, load spacing[, stages]". D = 64 has
-// a second configuration for sequences of at least FA2_D64_LONG_S (the LONG
-// tile): 32-key tiles at four waves per SIMD, 2-4% faster there and up to
-// 20% slower on short sequences.
-template <int W, int RB, int BC, int WPS, int LE, int NST = 2> struct TileCfg {
+// "waves, row blocks, keys, waves per SIMD, load spacing[, stages[,
+// pipelined]]". D = 64 has a second configuration for sequences of at least
+// FA2_D64_LONG_S (the LONG tile): 32-key tiles at four waves per SIMD, 2-4%
+// faster there and up to 20% slower on short sequences.
+template <int W, int RB, int BC, int WPS, int LE, int NST = 2, int PIPE = 1> struct TileCfg {
   static constexpr int kWaves = W, kRowBlocks = RB, kBc = BC, kWavesPerSimd = WPS, kLoadEvery = LE,
-                       kStages = NST;
+                       kStages = NST, kPipelined = PIPE;
 };
 #ifndef FA2_TILE_D64
 #define FA2_TILE_D64 4, 1, 64, 2, 1
@@ -56,7 +62,7 @@ template <int W, int RB, int BC, int WPS, int LE, int NST = 2> struct TileCfg {
 #define FA2_TILE_D128 4, 1, 64, 2, 2
 #endif
 #ifndef FA2_TILE_D256
-#define FA2_TILE_D256 4, 1, 64, 1, 1, 2
+#define FA2_TILE_D256 4, 1, 32, 2, 1, 2, 0
 #endif
 template <int D, bool LONG = false> struct Tile;
 template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};
@@ -75,6 +81,7 @@ template <int D, bool LONG = false> struct Shape {
   static constexpr int kTileBytes = kBc * D * 2;     // one K or one V tile
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per K (or V) tile
   static constexpr int kStages = Tile<D, LONG>::kStages;
+  static constexpr bool kPipelined = Tile<D, LONG>::kPipelined != 0;
   static constexpr int kLdsBytes = 2 * kStages * kTileBytes;  // K ring + V ring
   static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
   static_assert(kStages >= 2 && (kStages - 2) * 2 * kLoadsPerWave < 64, "ring depth");

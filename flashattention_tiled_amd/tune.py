@@ -3,7 +3,8 @@ cookbook notebook's exercise "Autotune BLOCK_M, BLOCK_N, num_warps".
 
 Each candidate sets one head dim's tile configuration (waves per workgroup,
 32-row blocks per wave, keys per tile, waves per SIMD, load spacing and,
-optionally, the depth of the K and V LDS rings (2 if absent); so
+optionally, the depth of the K and V LDS rings (2 if absent) and whether the
+key loop is pipelined (1 if absent); so
 B_r = 32 * waves * row blocks and B_c = keys per tile) through the
 FA2_TILE_D<D> macro of csrc/fa2_plan.h and is built into a library of its
 own (without the library's switch to its long-sequence D = 64 tile, so that
@@ -35,17 +36,17 @@ import time
 
 from .build import CSRC, HIP_FLAGS, HIPCC, INCLUDE, ROOT, SOURCES
 
-# (waves, row blocks, keys per tile, waves per SIMD, load spacing[, stages]);
-# the first entry of each list is the library default
+# (waves, row blocks, keys per tile, waves per SIMD, load spacing[, stages[,
+# pipelined]]); the first entry of each list is the library default
 CANDIDATES = {
     64: [(4, 1, 64, 2, 1), (4, 1, 64, 2, 0), (4, 1, 64, 2, 2), (4, 1, 32, 4, 0),
          (4, 1, 32, 2, 0), (8, 1, 64, 2, 0), (2, 1, 64, 2, 0), (4, 2, 64, 1, 0),
          (4, 1, 128, 1, 0)],
     128: [(4, 1, 64, 2, 2), (4, 1, 64, 2, 0), (4, 1, 64, 2, 1), (4, 1, 64, 2, 4),
           (8, 1, 64, 2, 2), (4, 1, 32, 2, 0), (2, 1, 64, 2, 1), (4, 1, 128, 1, 2)],
-    256: [(4, 1, 64, 1, 1, 2), (4, 1, 64, 1, 2, 2), (4, 1, 64, 1, 0, 2), (4, 1, 32, 1, 1, 4),
-          (4, 1, 32, 1, 0), (4, 1, 32, 1, 1), (4, 1, 32, 1, 0, 4), (4, 1, 32, 1, 2, 4),
-          (4, 1, 32, 1, 1, 3), (8, 1, 32, 1, 0), (2, 1, 32, 1, 0)],
+    256: [(4, 1, 32, 2, 1, 2, 0), (4, 1, 32, 2, 0, 2, 0), (4, 1, 32, 2, 2, 2, 0),
+          (8, 1, 32, 2, 1, 2, 0), (8, 1, 32, 2, 1, 4, 0), (4, 1, 64, 1, 1, 2),
+          (4, 1, 64, 1, 2, 2), (4, 1, 32, 1, 1, 4), (4, 1, 32, 1, 0, 4)],
 }
 
 
@@ -53,6 +54,8 @@ def valid(D: int, cfg) -> bool:
     """The kernel's compile-time conditions on a configuration."""
     w, rb, bc, wps, le = cfg[:5]
     stages = cfg[5] if len(cfg) > 5 else 2
+    if len(cfg) > 6 and cfg[6] not in (0, 1):
+        return False
     tile_bytes = bc * D * 2
     if (bc % 32 or tile_bytes % (1024 * w) or 2 * stages * tile_bytes > 160 * 1024
             or w * 64 > 1024 or stages < 2):
@@ -66,7 +69,8 @@ def valid(D: int, cfg) -> bool:
 
 def name(D: int, cfg) -> str:
     st = f"_st{cfg[5]}" if len(cfg) > 5 else ""
-    return f"d{D}_w{cfg[0]}_rb{cfg[1]}_bc{cfg[2]}_wps{cfg[3]}_le{cfg[4]}{st}"
+    serial = "_serial" if len(cfg) > 6 and cfg[6] == 0 else ""
+    return f"d{D}_w{cfg[0]}_rb{cfg[1]}_bc{cfg[2]}_wps{cfg[3]}_le{cfg[4]}{st}{serial}"
 
 
 def _build_one(out: str, D: int, cfg) -> tuple:

@@ -36,6 +36,9 @@ def test_validity_rule():
     assert not tune.valid(256, (4, 1, 32, 1, 1, 5))
     assert not tune.valid(256, (4, 1, 32, 1, 1, 6))
     assert not tune.valid(128, (4, 1, 64, 2, 2, 1))
+    # the key loop is pipelined (1) or not (0)
+    assert tune.valid(256, (4, 1, 32, 2, 1, 2, 0))
+    assert not tune.valid(256, (4, 1, 32, 2, 1, 2, 2))
 
 
 def test_names_are_unique():
