@@ -382,12 +382,12 @@ struct Strides {
   long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
 };
 
-template <int D, int DT, bool CAUSAL, bool STRIDED, bool LONG>
-__global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesPerSimd)) void fa2_fwd_kernel(
+template <int D, int DT, bool CAUSAL, bool STRIDED, bool ALT>
+__global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPerSimd)) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int S, float c /* scale * log2(e) */, int pair_split, Strides st, KeySplit ks) {
-  using SH = Shape<D, LONG>;
+  using SH = Shape<D, ALT>;
   using E = Elem<DT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
   constexpr int CPR = SH::kChunksPerRow, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
@@ -396,8 +396,11 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   constexpr int NDB = D / 32;   // 32-wide head-dim blocks of O^T
 
   constexpr int NST = SH::kStages;
+  constexpr int KG = SH::kKeyGroups, GW = SH::kGroupWaves;
+  static_assert(KG == 1 || RB == 1, "key groups take one row block per wave");
 
-  // K ring (stages 0 .. NST - 1) then V ring (stages 0 .. NST - 1), TB bytes each.
+  // Per key group: a K ring (stages 0 .. NST - 1) then a V ring (stages
+  // 0 .. NST - 1), TB bytes each.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SH::kLdsBytes];
   constexpr uint32_t kK0 = 0, kK1 = TB, kV0 = NST * TB, kV1 = (NST + 1) * TB;
 
@@ -405,6 +408,11 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   const int lane = tid & 63;
   const int wave = wave_uniform(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
+  // the wave's key group and its place in the group, which fixes its rows
+  // and its share of the group's tile loads
+  const int grp = KG > 1 ? wave_uniform(wave / GW) : 0;
+  const int gw = KG > 1 ? wave_uniform(wave % GW) : wave;
+  unsigned char* const ring = smem + grp * SH::kRingBytes;
 
   // Workgroup -> (query tile, batch*head). Tiles are taken in descending
   // query-tile order across all heads, so under causal masking the longest
@@ -430,7 +438,7 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   // chunks of this query tile (more than one: the rows leave partials)
   const int n_chunks = ks.ct == 0 ? 1 : CAUSAL ? qt / ks.m + 1 : ks.n_split;
   const int q0 = qt * Br;
-  const int wave_row0 = q0 + wave * SH::kRowsPerWave;
+  const int wave_row0 = q0 + gw * SH::kRowsPerWave;
 
   // This (b, h)'s Q, K, V and O, as element offsets from the base pointers,
   // their row strides in elements, and K's and V's row strides in bytes.
@@ -472,11 +480,11 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   const unsigned char* v_head = (const unsigned char*)(v + v_at);
   uint32_t k_off[LPW], v_off[LPW];
   if constexpr (STRIDED) {
-    tile_load_offsets_strided<D, LPW, false>(wave, lane, k_rb, k_off);
-    tile_load_offsets_strided<D, LPW, true>(wave, lane, v_rb, v_off);
+    tile_load_offsets_strided<D, LPW, false>(gw, lane, k_rb, k_off);
+    tile_load_offsets_strided<D, LPW, true>(gw, lane, v_rb, v_off);
   } else {
-    tile_load_offsets<D, LPW, false>(wave, lane, k_off);
-    tile_load_offsets<D, LPW, true>(wave, lane, v_off);
+    tile_load_offsets<D, LPW, false>(gw, lane, k_off);
+    tile_load_offsets<D, LPW, true>(gw, lane, v_off);
   }
   // buffer for key tile t of K or V (limit 0: a tile that is not needed,
   // whose loads return zero)
@@ -515,12 +523,28 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
   const int kv_end = CAUSAL ? min(q0 + Br, S) : S;
   const int t_all = (kv_end + Bc - 1) / Bc;
   const int t_stop = ks.ct > 0 ? min(t_all, t0 + ks.ct) : t_all;
-  const int n_tiles = t_stop - t0;  // tiles the workgroup loads, from t0
+  // The key tiles of this wave's group, g_t0 .. g_stop - 1. With two key
+  // groups, group 0 takes the first h tiles and group 1 the rest (under
+  // causal masking, the diagonal ones). h is at most the number of tiles
+  // that end at or before the query tile's first row, so that the first
+  // tile of either group holds a key for every row; for the first query
+  // tile that is none, and group 1 takes them all. Both groups run n_steps
+  // pipeline steps (the shorter one's last step only loads zeros) so that
+  // they meet at every barrier.
+  int g_t0 = t0, g_stop = t_stop, n_steps = t_stop - t0, h_split = 0;
+  if constexpr (KG > 1) {
+    const int n = t_stop - t0;
+    h_split = CAUSAL ? min(n / 2, q0 / Bc - t0) : n / 2;
+    g_t0 = grp ? t0 + h_split : t0;
+    g_stop = grp ? t_stop : t0 + h_split;
+    n_steps = max(h_split, n - h_split);
+  }
+  const int n_tiles = g_stop - g_t0;  // tiles the group loads, from g_t0
   // tiles this wave computes (under causal masking the later tiles of the
-  // workgroup lie wholly above this wave's rows); at least one, as t0 B_c
-  // is at most the tile's first row
+  // workgroup lie wholly above this wave's rows); at least one when the
+  // group has any, as g_t0 B_c is at most the tile's first row
   const int n_act =
-      CAUSAL ? min(t_stop, (wave_row0 + SH::kRowsPerWave + Bc - 1) / Bc) - t0 : n_tiles;
+      CAUSAL ? min(g_stop, (wave_row0 + SH::kRowsPerWave + Bc - 1) / Bc) - g_t0 : n_tiles;
 
   // Software pipeline. Iteration j computes the scores of tile j + 1 on the
   // matrix cores while the vector unit turns tile j's scores into P, then the
@@ -537,20 +561,20 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     // is done with iteration j - 1, whose stage then takes tile j + NST - 1.
 #pragma unroll
     for (int i = 0; i + 1 < NST; ++i) {
-      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, t0 + i), smem + kK0 + i * TB, wave, k_off);
-      load_tile_rsrc<LPW>(v_tile(i < n_tiles ? S : 0, t0 + i), smem + kV0 + i * TB, wave, v_off);
+      load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, g_t0 + i), ring + kK0 + i * TB, gw, k_off);
+      load_tile_rsrc<LPW>(v_tile(i < n_tiles ? S : 0, g_t0 + i), ring + kV0 + i * TB, gw, v_off);
     }
     auto step_s = [&](auto sj_c, int j) {
       constexpr int SJ = decltype(sj_c)::value, SF = (SJ + NST - 1) % NST;
       wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
       workgroup_barrier();
       const int tn = j + NST - 1;
-      const StepLoads<LPW> ld{k_tile(tn < n_tiles ? S : 0, t0 + tn),
-                              v_tile(tn < n_tiles ? S : 0, t0 + tn),
-                              smem + kK0 + SF * TB, smem + kV0 + SF * TB, k_off, v_off, wave};
+      const StepLoads<LPW> ld{k_tile(tn < n_tiles ? S : 0, g_t0 + tn),
+                              v_tile(tn < n_tiles ? S : 0, g_t0 + tn),
+                              ring + kK0 + SF * TB, ring + kV0 + SF * TB, k_off, v_off, gw};
       if (j < n_act) {
-        serial_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery, CAUSAL>(
-            ld, smem, kK0 + SJ * TB, kV0 + SJ * TB, k_lane, vt_x, qf, (t0 + j) * Bc, wave_row0,
+        serial_block<D, DT, RB, NKB, LPW, Tile<D, ALT>::kLoadEvery, CAUSAL>(
+            ld, ring, kK0 + SJ * TB, kV0 + SJ * TB, k_lane, vt_x, qf, (g_t0 + j) * Bc, wave_row0,
             S, c, l32, hi, j == 0, m_run, l_run, l_rnd, acc_o);
       } else {
 #pragma unroll
@@ -560,9 +584,9 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     auto step_su = [&](auto u, int j0) {
       constexpr int UU = decltype(u)::value;
       if constexpr (UU < NST)
-        if (UU == 0 || j0 + UU < n_tiles) step_s(std::integral_constant<int, UU>{}, j0 + UU);
+        if (UU == 0 || j0 + UU < n_steps) step_s(std::integral_constant<int, UU>{}, j0 + UU);
     };
-    for (int j = 0; j < n_tiles; j += NST) {
+    for (int j = 0; j < n_steps; j += NST) {
       step_su(std::integral_constant<int, 0>{}, j);
       step_su(std::integral_constant<int, 1>{}, j);
       step_su(std::integral_constant<int, 2>{}, j);
@@ -570,19 +594,19 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     }
     static_assert(NST <= 4, "unroll");
   } else {
-    load_tile_rsrc<LPW>(k_tile(S, t0), smem + kK0, wave, k_off);
+    load_tile_rsrc<LPW>(k_tile(n_tiles > 0 ? S : 0, g_t0), ring + kK0, gw, k_off);
     if constexpr (NST == 2) {
-      load_tile_rsrc<LPW>(v_tile(S, t0), smem + kV0, wave, v_off);
-      if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, t0 + 1), smem + kK1, wave, k_off);
+      load_tile_rsrc<LPW>(v_tile(n_tiles > 0 ? S : 0, g_t0), ring + kV0, gw, v_off);
+      if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, g_t0 + 1), ring + kK1, gw, k_off);
     } else {
       // the loads iterations 1 - NST .. -1 would have issued, K then V of each
       // (a tile past the workgroup's last gets a zero-length buffer)
 #pragma unroll
       for (int i = 1; i < NST; ++i) {
-        load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, t0 + i), smem + kK0 + i * TB, wave,
+        load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, g_t0 + i), ring + kK0 + i * TB, gw,
                             k_off);
-        load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? S : 0, t0 + i - 1),
-                            smem + kV0 + (i - 1) * TB, wave, v_off);
+        load_tile_rsrc<LPW>(v_tile(i - 1 < n_tiles ? S : 0, g_t0 + i - 1),
+                            ring + kV0 + (i - 1) * TB, gw, v_off);
       }
     }
 
@@ -593,10 +617,10 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     wait_vm_lgkm0<0>();
     workgroup_barrier();
     if (n_act > 0) {
-      // m starts at the row max of tile t0, which holds an unmasked key for
-      // every row (key t0 B_c <= q0), so m is finite from here on
-      tile_scores<D, DT, RB, NKB>(smem, kK0, k_lane, qf, s_a);
-      tile_mask<RB, NKB, CAUSAL>(s_a, t0 * Bc, wave_row0, S, c, l32, hi, ce_a);
+      // m starts at the row max of tile g_t0, which holds an unmasked key
+      // for every row (key g_t0 B_c <= q0), so m is finite from here on
+      tile_scores<D, DT, RB, NKB>(ring, kK0, k_lane, qf, s_a);
+      tile_mask<RB, NKB, CAUSAL>(s_a, g_t0 * Bc, wave_row0, S, c, l32, hi, ce_a);
       tile_max<RB, NKB>(s_a, ce_a, m_run);
     }
 
@@ -627,19 +651,20 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
       // workgroup's last gets a zero-length buffer, so its loads only write
       // zeros to a free stage
       const StepLoads<LPW> ld{
-          k_tile(j + NST < n_tiles ? S : 0, t0 + j + NST),
-          v_tile(j + NST - 1 < n_tiles ? S : 0, t0 + j + NST - 1),
-          smem + k_free, smem + v_free, k_off, v_off, wave};
+          k_tile(j + NST < n_tiles ? S : 0, g_t0 + j + NST),
+          v_tile(j + NST - 1 < n_tiles ? S : 0, g_t0 + j + NST - 1),
+          ring + k_free, ring + v_free, k_off, v_off, gw};
       if (j < n_act) {
         // scores of tile j + 1 || probabilities of tile j, then P V of tile j
         // (past the wave's last tile the scores come from a stale stage and are
         // never used)
-        pipeline_block<D, DT, RB, NKB, LPW, Tile<D, LONG>::kLoadEvery>(
-            ld, smem, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt,
+        pipeline_block<D, DT, RB, NKB, LPW, Tile<D, ALT>::kLoadEvery>(
+            ld, ring, k_next, v_cur, k_lane, vt_x, qf, cur, ce_cur, m_run, l_run, l_rnd, nxt,
             acc_o);
         if (j + 1 < n_act) {
-          if (tile_needs_mask<RB, NKB, CAUSAL>((t0 + j + 1) * Bc, wave_row0, S)) {
-            tile_mask<RB, NKB, CAUSAL>(nxt, (t0 + j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
+          if (tile_needs_mask<RB, NKB, CAUSAL>((g_t0 + j + 1) * Bc, wave_row0, S)) {
+            tile_mask<RB, NKB, CAUSAL>(nxt, (g_t0 + j + 1) * Bc, wave_row0, S, c, l32, hi,
+                                       ce_nxt);
           } else {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) ce_nxt[rb] = c;
@@ -655,7 +680,7 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     auto step_u = [&](auto u, int j0) {
       constexpr int UU = decltype(u)::value;
       if constexpr (UU < U) {
-        if (UU == 0 || j0 + UU < n_tiles) {
+        if (UU == 0 || j0 + UU < n_steps) {
           if constexpr (UU % 2 == 0)
             step(std::integral_constant<int, 0>{}, std::integral_constant<int, UU % NST>{}, j0 + UU,
                  s_a, ce_a, s_b, ce_b);
@@ -665,7 +690,7 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
         }
       }
     };
-    for (int j = 0; j < n_tiles; j += U) {
+    for (int j = 0; j < n_steps; j += U) {
       step_u(std::integral_constant<int, 0>{}, j);
       step_u(std::integral_constant<int, 1>{}, j);
       step_u(std::integral_constant<int, 2>{}, j);
@@ -676,8 +701,45 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
     static_assert(U <= 6, "unroll");
   }
   // the last steps' loads (zeros into free stages) must land before the
-  // workgroup's LDS is released
+  // workgroup's LDS is released (or reused for the merge)
   wait_vm_lgkm0<0>();
+
+  if constexpr (KG > 1) {
+    // Merge the key groups' partial results for each row, as the pages'
+    // split of a row's keys into parts merges them: both are rescaled to the
+    // larger reference max, O~ and both sums added. Group 1 stores its O~,
+    // m, l and l' in the LDS the rings leave free, lane by lane (lane l of
+    // wave w of either group holds the same elements); group 0 combines them
+    // with its own (or takes them over when it had no tiles) and writes the
+    // rows.
+    workgroup_barrier();
+    float* mg = (float*)smem + (size_t)gw * SH::kMergeFloats * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mg[(db * 16 + r) * 64] = acc_o[0][db][r];
+      mg[(NDB * 16) * 64] = m_run[0];
+      mg[(NDB * 16 + 1) * 64] = l_run[0];
+      mg[(NDB * 16 + 2) * 64] = l_rnd[0];
+    }
+    workgroup_barrier();
+    if (grp == 1) return;
+    const float m1 = mg[(NDB * 16) * 64];
+    const float l1 = mg[(NDB * 16 + 1) * 64], lr1 = mg[(NDB * 16 + 2) * 64];
+    // group 0 without tiles: weight 0 for its (unset) state
+    const float m_new = h_split > 0 ? fmaxf(m_run[0], m1) : m1;
+    const float a0 = h_split > 0 ? __builtin_amdgcn_exp2f(m_run[0] - m_new) : 0.f;
+    const float a1 = __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc_o[0][db][r] = acc_o[0][db][r] * a0 + mg[(db * 16 + r) * 64] * a1;
+    m_run[0] = m_new;
+    l_run[0] = l_run[0] * a0 + l1 * a1;
+    l_rnd[0] = l_rnd[0] * a0 + lr1 * a1;
+  }
 
   // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, and
   // lse = ln2 (m + log2 l) from the unrounded sum; or, for one chunk of a
@@ -721,11 +783,11 @@ __global__ __launch_bounds__((Shape<D, LONG>::kThreads), (Tile<D, LONG>::kWavesP
 // Launch the kernel over (B, H, S); `st` gives the strides of a strided call
 // (nullptr: contiguous tensors), `ks` a key split (ct = 0: none), whose
 // merge follows on the same stream.
-template <int D, int DT, bool CAUSAL, bool LONG>
+template <int D, int DT, bool CAUSAL, bool ALT>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int S, float scale, const Strides* st, const KeySplit& ks, int n_cu,
                   hipStream_t stream) {
-  using SH = Shape<D, LONG>;
+  using SH = Shape<D, ALT>;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
   // work items per (b, h): query tiles, or their key chunks under a split
   const int n_x = (int)split_items_per_head(ks, n_qt, CAUSAL);
@@ -733,7 +795,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const dim3 block(SH::kThreads);
   // workgroups resident per compute unit: the register budget allows
   // kWavesPerSimd waves per SIMD, i.e. that many 4-wave workgroups
-  const long long slots = (long long)n_cu * Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long slots = (long long)n_cu * Tile<D, ALT>::kWavesPerSimd * 4 / SH::kWaves;
   const long long n_wg = (long long)n_qt * H * B;
   const int pair_split = (CAUSAL && ks.ct == 0 && n_qt > 1 && n_wg <= slots)
                              ? (int)(((n_qt + 1) / 2) * (long long)H * B)
@@ -742,11 +804,11 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
                    (long long)S * D,     D,                 (long long)H * S * D, (long long)S * D,
                    D,                    (long long)H * S * D, (long long)S * D, D};
   if (st)
-    fa2_fwd_kernel<D, DT, CAUSAL, true, LONG><<<grid, block, 0, stream>>>(
+    fa2_fwd_kernel<D, DT, CAUSAL, true, ALT><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
         scale * kLog2e, pair_split, *st, ks);
   else
-    fa2_fwd_kernel<D, DT, CAUSAL, false, LONG><<<grid, block, 0, stream>>>(
+    fa2_fwd_kernel<D, DT, CAUSAL, false, ALT><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
         scale * kLog2e, pair_split, cs, ks);
   hipError_t err = hipGetLastError();
@@ -756,18 +818,18 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
                                CAUSAL ? ks.row0 : 0, ks.n_split, os.ob, os.oh, os.os, stream);
 }
 
-template <int D, bool LONG>
+template <int D, bool ALT>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                         void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
                         const KeySplit& ks, int n_cu, hipStream_t stream) {
   if (dtype == FA2_F16)
-    return causal ? launch<D, FA2_F16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
+    return causal ? launch<D, FA2_F16, true, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
                                                    stream)
-                  : launch<D, FA2_F16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
+                  : launch<D, FA2_F16, false, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
                                                     stream);
-  return causal ? launch<D, FA2_BF16, true, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
+  return causal ? launch<D, FA2_BF16, true, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
                                                   stream)
-                : launch<D, FA2_BF16, false, LONG>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
+                : launch<D, FA2_BF16, false, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
                                                    stream);
 }
 
@@ -782,8 +844,11 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
                  : launch_dtype<64, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
                                            n_cu, stream);
     case 128:
-      return launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                      n_cu, stream);
+      return d128_alt(B, H, S, causal != 0, ks.ct > 0, n_cu)
+                 ? launch_dtype<128, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                           n_cu, stream)
+                 : launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st,
+                                            ks, n_cu, stream);
     default:
       return launch_dtype<256, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
                                       n_cu, stream);
@@ -792,8 +857,10 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
 
 }  // namespace
 
-static_assert(Shape<64, true>::kBr == Shape<64>::kBr,
-              "both D = 64 tiles take the query rows per workgroup fa2_rows_per_workgroup reports");
+static_assert(Shape<64, true>::kBr == Shape<64>::kBr &&
+                  (FA2_D128_ALT == 0 || Shape<128, true>::kBr == Shape<128>::kBr),
+              "both tiles of a head dim (where both are used) take the query rows per "
+              "workgroup fa2_rows_per_workgroup reports");
 
 extern "C" int fa2_rows_per_workgroup(int D) {
   switch (D) {

@@ -31,6 +31,12 @@ namespace {
 //                  softmax (two score buffers); 0: scores, softmax and P V of
 //                  tile j in sequence, one score buffer, and the other waves
 //                  of the SIMD fill the gaps (for registers too tight for two)
+//   kKeyGroups     groups of kWaves / kKeyGroups waves that split the key
+//                  tiles of one query tile between them (default 1). Each
+//                  group owns all B_r rows and streams its own key range
+//                  through its own rings; at the end the groups' (m, l, O~)
+//                  are merged through LDS, as the pages' split of the keys
+//                  across warps merges them.
 // Pipelined, iteration j reads K of tile j + 1 and V of tile j while K of
 // tile j + kStages and V of tile j + kStages - 1 load; unpipelined, it reads
 // K and V of tile j while those of tile j + kStages - 1 load. Either way a
@@ -42,12 +48,20 @@ namespace {
 // The defaults are the best of a sweep over these values on the benchmark
 // shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides one, as
 // "waves, row blocks, keys, waves per SIMD, load spacing[, stages[,
-// pipelined]]". D = 64 has a second configuration for sequences of at least
-// FA2_D64_LONG_S (the LONG tile): 32-key tiles at four waves per SIMD, 2-4%
-// faster there and up to 20% slower on short sequences.
-template <int W, int RB, int BC, int WPS, int LE, int NST = 2, int PIPE = 1> struct TileCfg {
+// pipelined[, key groups]]]". D = 64 and D = 128 have a second (ALT)
+// configuration. D = 64's is for sequences of at least FA2_D64_LONG_S:
+// 32-key tiles at four waves per SIMD, 2-4% faster there and up to 20%
+// slower on short sequences. D = 128's is for causal grids whose workgroups
+// of the main tile are all resident at once (d128_alt): there the longest
+// query tiles set the time, run at one wave per SIMD once their compute
+// unit's other workgroup is done (or from the start, at one workgroup per
+// unit). The ALT tile splits each query tile's keys between two groups of
+// four waves, one workgroup per unit, so that every query tile runs at two
+// waves per SIMD to its end and the units take the tiles longest first.
+template <int W, int RB, int BC, int WPS, int LE, int NST = 2, int PIPE = 1, int KG = 1>
+struct TileCfg {
   static constexpr int kWaves = W, kRowBlocks = RB, kBc = BC, kWavesPerSimd = WPS, kLoadEvery = LE,
-                       kStages = NST, kPipelined = PIPE;
+                       kStages = NST, kPipelined = PIPE, kKeyGroups = KG;
 };
 #ifndef FA2_TILE_D64
 #define FA2_TILE_D64 4, 1, 64, 2, 1
@@ -61,29 +75,42 @@ template <int W, int RB, int BC, int WPS, int LE, int NST = 2, int PIPE = 1> str
 #ifndef FA2_TILE_D128
 #define FA2_TILE_D128 4, 1, 64, 2, 2
 #endif
+#ifndef FA2_TILE_D128_ALT
+#define FA2_TILE_D128_ALT 8, 1, 64, 2, 2, 2, 1, 2
+#endif
 #ifndef FA2_TILE_D256
 #define FA2_TILE_D256 4, 1, 32, 2, 1, 2, 0
 #endif
-template <int D, bool LONG = false> struct Tile;
+template <int D, bool ALT = false> struct Tile;
 template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};
 template <> struct Tile<64, true> : TileCfg<FA2_TILE_D64_LONG> {};
 template <> struct Tile<128> : TileCfg<FA2_TILE_D128> {};
+template <> struct Tile<128, true> : TileCfg<FA2_TILE_D128_ALT> {};
 template <> struct Tile<256> : TileCfg<FA2_TILE_D256> {};
 
-template <int D, bool LONG = false> struct Shape {
-  static constexpr int kWaves = Tile<D, LONG>::kWaves;
+template <int D, bool ALT = false> struct Shape {
+  static constexpr int kWaves = Tile<D, ALT>::kWaves;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRB = Tile<D, LONG>::kRowBlocks;
+  static constexpr int kKeyGroups = Tile<D, ALT>::kKeyGroups;
+  static constexpr int kGroupWaves = kWaves / kKeyGroups;  // waves of one key group
+  static constexpr int kRB = Tile<D, ALT>::kRowBlocks;
   static constexpr int kRowsPerWave = 32 * kRB;
-  static constexpr int kBr = kWaves * kRowsPerWave;  // query rows per workgroup
-  static constexpr int kBc = Tile<D, LONG>::kBc;
+  static constexpr int kBr = kGroupWaves * kRowsPerWave;  // query rows per workgroup
+  static constexpr int kBc = Tile<D, ALT>::kBc;
   static constexpr int kChunksPerRow = D / 8;        // 16-byte chunks per key row
   static constexpr int kTileBytes = kBc * D * 2;     // one K or one V tile
-  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;  // per K (or V) tile
-  static constexpr int kStages = Tile<D, LONG>::kStages;
-  static constexpr bool kPipelined = Tile<D, LONG>::kPipelined != 0;
-  static constexpr int kLdsBytes = 2 * kStages * kTileBytes;  // K ring + V ring
-  static_assert(kTileBytes % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+  static constexpr int kLoadsPerWave = kTileBytes / 1024 / kGroupWaves;  // per K (or V) tile
+  static constexpr int kStages = Tile<D, ALT>::kStages;
+  static constexpr bool kPipelined = Tile<D, ALT>::kPipelined != 0;
+  static constexpr int kRingBytes = 2 * kStages * kTileBytes;  // one group's K ring + V ring
+  // the merge of the key groups: a group's O~ (D / 2 floats per lane) and
+  // its m, l and l' per lane, for each of its waves, laid out lane-major
+  static constexpr int kMergeFloats = D / 2 + 3;
+  static constexpr int kMergeBytes = kKeyGroups > 1 ? kGroupWaves * kMergeFloats * 64 * 4 : 0;
+  static constexpr int kLdsBytes =
+      kKeyGroups * kRingBytes > kMergeBytes ? kKeyGroups * kRingBytes : kMergeBytes;
+  static_assert(kWaves % kKeyGroups == 0 && kKeyGroups <= 2, "key groups");
+  static_assert(kTileBytes % (1024 * kGroupWaves) == 0, "tile must split into 1 KiB wave loads");
   static_assert(kStages >= 2 && (kStages - 2) * 2 * kLoadsPerWave < 64, "ring depth");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
@@ -200,15 +227,15 @@ constexpr double kSplitMargin = 1.5;
 // and at least all its work at the whole GPU's rate; the split is taken
 // when the time it saves by that estimate beats the merge's cost by
 // kSplitMargin.
-template <int D, bool LONG>
+template <int D, bool ALT>
 KeySplit plan_split_for(int B, int H, int S, bool causal, int n_cu) {
-  using SH = Shape<D, LONG>;
+  using SH = Shape<D, ALT>;
   KeySplit ks{};
   const long long Br = SH::kBr, Bc = SH::kBc, rho = Br / Bc;
-  const long long slots = (long long)n_cu * Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long slots = (long long)n_cu * Tile<D, ALT>::kWavesPerSimd * 4 / SH::kWaves;
   const long long n_qt = (S + Br - 1) / Br, n_bh = (long long)B * H, n_t = (S + Bc - 1) / Bc;
   const long long n_wg = n_qt * n_bh;
-  const bool one_per_cu = Tile<D, LONG>::kWavesPerSimd * 4 / SH::kWaves < 2;
+  const bool one_per_cu = Tile<D, ALT>::kWavesPerSimd * 4 / SH::kWaves < 2;
   const long long max_wg = !causal ? n_cu / 2 : one_per_cu ? slots : slots / 2;
   if (slots < 1 || n_qt < 2 || n_wg > max_wg) return ks;
   long long ct, m = 0, n_split, row0;
@@ -261,6 +288,23 @@ KeySplit plan_split_for(int B, int H, int S, bool causal, int n_cu) {
   ks.row0 = (int)row0;
   ks.n_qt = (int)n_qt;
   return ks;
+}
+
+// Whether a D = 128 launch takes the ALT tile (key groups): causal, not
+// split, and the main tile's workgroups all resident at once with at least
+// one per compute unit (with fewer, the tiles are short and the split of
+// their keys does not pay for the merge). FA2_D128_ALT overrides the rule:
+// 0 never, 2 whenever not split.
+#ifndef FA2_D128_ALT
+#define FA2_D128_ALT 1
+#endif
+bool d128_alt(int B, int H, int S, bool causal, bool split, int n_cu) {
+  using SH = Shape<128>;
+  if (FA2_D128_ALT == 0 || split) return false;
+  if (FA2_D128_ALT == 2) return true;
+  const long long slots = (long long)n_cu * Tile<128>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long n_wg = (long long)((S + SH::kBr - 1) / SH::kBr) * B * H;
+  return causal && n_wg >= n_cu && n_wg <= slots;
 }
 
 KeySplit plan_split(int D, int B, int H, int S, bool causal, int n_cu) {

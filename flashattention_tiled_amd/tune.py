@@ -4,16 +4,15 @@ cookbook notebook's exercise "Autotune BLOCK_M, BLOCK_N, num_warps".
 Each candidate sets one head dim's tile configuration (waves per workgroup,
 32-row blocks per wave, keys per tile, waves per SIMD, load spacing and,
 optionally, the depth of the K and V LDS rings (2 if absent) and whether the
-key loop is pipelined (1 if absent); so
-B_r = 32 * waves * row blocks and B_c = keys per tile) through the
-FA2_TILE_D<D> macro of csrc/fa2_plan.h and is built into a library of its
-own (without the library's switch to its long-sequence D = 64 tile, so that
-the candidate itself runs at every length). On a GPU, every library runs every
-benchmark shape of its head dim in
-fp16 and bf16: first a check that its output agrees with the default
-library's (both are within the parity tolerance of exact attention, so they
-agree within twice it), then the timing. The library defaults are the best
-configurations found this way.
+key loop is pipelined (1 if absent); so B_r = 32 * waves * row blocks and
+B_c = keys per tile) through the FA2_TILE_D<D> macro of csrc/fa2_plan.h and
+is built into a library of its own (without the library's switches to its
+long-sequence D = 64 tile and its key-group D = 128 tile, so that the
+candidate itself runs at every shape). On a GPU, every library runs every
+benchmark shape of its head dim in fp16 and bf16: first a check that its
+output agrees with the default library's (both are within the parity
+tolerance of exact attention, so they agree within twice it), then the
+timing. The library defaults are the best configurations found this way.
 
     python -m flashattention_tiled_amd.tune build [--out DIR] [--jobs N]
     python -m flashattention_tiled_amd.tune run [--out DIR] [--csv PATH] [--steps K]
@@ -76,10 +75,10 @@ def name(D: int, cfg) -> str:
 def _build_one(out: str, D: int, cfg) -> tuple:
     path = os.path.join(out, f"libfa2_{name(D, cfg)}.so")
     val = ",".join(str(x) for x in cfg)
-    # the candidate runs at every S: no switch to the long-sequence D = 64
+    # the candidate runs at every shape: no switch to the long-sequence D = 64
     # tile, which takes the candidate's configuration too (both D = 64 tiles
-    # must have one B_r)
-    macros = [f"-DFA2_TILE_D{D}={val}", "-DFA2_D64_LONG_S=2147483647"]
+    # must have one B_r), nor to D = 128's key-group tile
+    macros = [f"-DFA2_TILE_D{D}={val}", "-DFA2_D64_LONG_S=2147483647", "-DFA2_D128_ALT=0"]
     if D == 64:
         macros.append(f"-DFA2_TILE_D64_LONG={val}")
     cmd = [HIPCC, *HIP_FLAGS, *macros, "-I", INCLUDE, "-I", CSRC, "-o", path, *SOURCES]

@@ -1,0 +1,64 @@
+"""The D = 128 tile that splits each query tile's keys between two wave
+groups (merged through LDS), against the fp64 oracle on every output.
+
+fa2_fwd takes it for causal D = 128 grids whose main-tile workgroups are all
+resident at once with at least one per compute unit (256 to 512 query tiles
+of 128 rows on the 256 units of an MI355X). The cases cover the split at
+every query tile, including the first (whose keys all go to the second
+group), ragged sequence ends inside a group's last tile, an odd number of
+key tiles (the groups run different numbers of tiles), both dtypes, a
+negative scale, strided views, and the shape beside it that keeps the main
+tile. Tolerances: max |dO| <= 2e-3 (fp16) / 1.6e-2 (bf16), lse relative
+error <= 1e-4.
+"""
+import math
+
+import pytest
+import torch
+
+import flashattention_tiled_amd as fa
+import workloads as wl
+from gpu_helpers import DEV, announce, assert_parity, oracle_full
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (B, H, S, dtype, scale sign): query tiles = ceil(S / 128) * B * H
+    (1, 40, 1000, "f16", 1),     # 320 tiles, ragged end inside a key tile
+    (2, 8, 4000, "bf16", 1),     # 512 tiles, 63 key tiles per long row block
+    (1, 4, 8192, "f16", 1),      # 256 tiles: one long head per 64 units
+    (1, 36, 960, "f16", -1),     # 288 tiles, negative scale
+    (1, 16, 2049, "bf16", 1),    # 272 tiles, a one-row last tile
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_key_groups_every_row(case):
+    B, H, S, dt, sign = case
+    w = wl.Workload("key_groups", B, H, S, 128, dt, True)
+    scale = sign / math.sqrt(128)
+    announce(f"key groups B={B} H={H} S={S} {dt} scale={scale:+.4f}")
+    q, k, v = wl.make_qkv(w, seed=S + H)
+    # fa2_fwd itself (attention() may take the key split of fa2_fwd_balanced)
+    o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale,
+                          balanced=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, True, scale)
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, dt, f"key groups {case}")
+
+
+def test_key_groups_strided():
+    """Q, K and V as views into one packed (B, S, 3, H, D) projection."""
+    B, H, S, D = 1, 48, 700, 128
+    announce(f"key groups strided B={B} H={H} S={S}")
+    w = wl.Workload("key_groups_strided", B, H, S, D, "f16", True)
+    q, k, v = wl.make_qkv(w, seed=7)
+    packed = torch.empty((B, S, 3, H, D), dtype=torch.float16, device=DEV)
+    packed[:, :, 0] = q.permute(0, 2, 1, 3).to(DEV)
+    packed[:, :, 1] = k.permute(0, 2, 1, 3).to(DEV)
+    packed[:, :, 2] = v.permute(0, 2, 1, 3).to(DEV)
+    qs, ks, vs = (packed[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+    o, lse = fa.attention(qs, ks, vs, causal=True, scale=w.scale, balanced=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, True, w.scale)
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, "f16", "key groups strided")
