@@ -468,11 +468,11 @@ def run_table(path: str, steps: int, warmup: int, with_oracle: bool = False):
     rows = []
     for w in wl.ALL:
         # fa2_fwd, fa2_fwd_balanced where it splits the keys of this shape,
-        # and fa2_fwd_fp8 (e4m3 inputs) where it has a kernel (D = 64, 128)
+        # and fa2_fwd_fp8 (e4m3 inputs)
         entries = ["fa2_fwd"]
         if fa.fa2_fwd_balanced_workspace_bytes(w.B, w.H, w.S, w.D, int(w.causal)) > 0:
             entries.append("fa2_fwd_balanced")
-        if w.D in (64, 128) and w not in wl.TINY:
+        if w not in wl.TINY:
             entries.append("fa2_fwd_fp8")
         for entry in entries:
             fp8 = entry == "fa2_fwd_fp8"

@@ -56,9 +56,12 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
 }
 
 // Tile shape of the FP8 kernel: 4 waves of 32 query rows, 64-key tiles,
-// two waves per SIMD, two-stage K and V rings.
+// two waves per SIMD, two-stage K and V rings. At D = 256 the key loop is
+// unpipelined (one score buffer: a second does not fit beside Q^T and O~ in
+// 256 registers), as in the 16-bit kernel.
 template <int D> struct Fp8Shape {
   static constexpr int kWaves = 4, kThreads = 256, kBr = 128, kBc = 64;
+  static constexpr bool kSerial = D == 256;
   static constexpr int kTileBytes = kBc * D;  // one K or V tile of codes
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;
   static constexpr int kLdsBytes = 4 * kTileBytes;  // K and V rings, two stages each
@@ -220,67 +223,110 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
     acc_l = mfma_fp8(ones, pb, acc_l);
   };
 
-  // prologue: K and V of tile 0 and K of tile 1
-  load_tile_rsrc<LPW>(k_tile(S, 0), smem + kK0, wave, k_off);
-  load_tile_rsrc<LPW>(v_tile(S, 0), smem + kV0, wave, v_off);
-  if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, 1), smem + kK1, wave, k_off);
-
-  f32x16 s_a[1][NKB], s_b[1][NKB];
-  float ce_a[1], ce_b[1];
-  wait_vm_lgkm0<0>();
-  workgroup_barrier();
-  if (n_act > 0) {
-    // m starts at the row max of tile 0, which holds key 0 <= every row
-    scores(kK0, s_a);
-    tile_mask<1, NKB, CAUSAL>(s_a, 0, wave_row0, S, c, l32, hi, ce_a);
-    m_run = fp8_tile_max<NKB>(s_a, ce_a[0]);
-  }
-
-  // One step for tile j (parity PAR): scores of tile j + 1 beside the
-  // probabilities of tile j, the headroom test, then P V of tile j.
-  auto step = [&](auto par, int j, f32x16 (&cur)[1][NKB], float (&ce_cur)[1],
-                  f32x16 (&nxt)[1][NKB], float (&ce_nxt)[1]) {
-    constexpr int PAR = decltype(par)::value;
-    const uint32_t k_next = PAR ? kK0 : kK1, k_free = PAR ? kK1 : kK0;
-    const uint32_t v_cur = PAR ? kV1 : kV0, v_free = PAR ? kV0 : kV1;
-    wait_vm_lgkm0<0>();
-    workgroup_barrier();
-    // K of tile j + 2 into tile j's K stage, V of tile j + 1 into tile
-    // j - 1's V stage (tiles past the last get zero-length buffers)
-    load_tile_rsrc<LPW>(k_tile(j + 2 < n_tiles ? S : 0, j + 2), smem + k_free, wave,
-                        k_off);
-    load_tile_rsrc<LPW>(v_tile(j + 1 < n_tiles ? S : 0, j + 1), smem + v_free, wave,
-                        v_off);
-    if (j < n_act) {
-      scores(k_next, nxt);
-      // the headroom test on tile j: raise m to the tile's row max first if
-      // any row of the wave needs it (rare, wave-uniform)
-      const float tmax = fp8_tile_max<NKB>(cur, ce_cur[0]);
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kP8Headroom) != 0) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        acc_l *= alpha;
+  // the headroom test on a tile's scores: raise m to the tile's row max
+  // first if any row of the wave needs it (rare, wave-uniform)
+  auto headroom = [&](const f32x16 (&sc)[1][NKB], float ce) {
+    const float tmax = fp8_tile_max<NKB>(sc, ce);
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kP8Headroom) != 0) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      acc_l *= alpha;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-        m_run = m_new;
-      }
-      float tsum;
-      i32x8 pb;
-      fp8_probs<NKB>(cur, ce_cur[0], m_run - (float)kP8Exp, tsum, pb);
-      l_run += tsum;
-      pv(v_cur, pb);
-      if (j + 1 < n_act) {
-        if (tile_needs_mask<1, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S))
-          tile_mask<1, NKB, CAUSAL>(nxt, (j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
-        else
-          ce_nxt[0] = c;
-      }
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      m_run = m_new;
     }
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j, s_a, ce_a, s_b, ce_b);
-    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1, s_b, ce_b, s_a, ce_a);
+
+  if constexpr (SH::kSerial) {
+    // Unpipelined: iteration j computes tile j from stage j % 2 (scores,
+    // headroom test, P8, P V) after its loads (issued in iteration j - 1)
+    // have landed and every wave is done with iteration j - 1, whose stages
+    // then take tile j + 1.
+    load_tile_rsrc<LPW>(k_tile(S, 0), smem + kK0, wave, k_off);
+    load_tile_rsrc<LPW>(v_tile(S, 0), smem + kV0, wave, v_off);
+    auto step_s = [&](auto par, int j) {
+      constexpr int PAR = decltype(par)::value;
+      const uint32_t k_cur = PAR ? kK1 : kK0, k_free = PAR ? kK0 : kK1;
+      const uint32_t v_cur = PAR ? kV1 : kV0, v_free = PAR ? kV0 : kV1;
+      wait_vm_lgkm0<0>();
+      workgroup_barrier();
+      load_tile_rsrc<LPW>(k_tile(j + 1 < n_tiles ? S : 0, j + 1), smem + k_free, wave, k_off);
+      load_tile_rsrc<LPW>(v_tile(j + 1 < n_tiles ? S : 0, j + 1), smem + v_free, wave, v_off);
+      if (j < n_act) {
+        f32x16 sc[1][NKB];
+        float ce[1];
+        scores(k_cur, sc);
+        if (tile_needs_mask<1, NKB, CAUSAL>(j * Bc, wave_row0, S))
+          tile_mask<1, NKB, CAUSAL>(sc, j * Bc, wave_row0, S, c, l32, hi, ce);
+        else
+          ce[0] = c;
+        // m starts at the row max of tile 0, which holds key 0 <= every row
+        if (j == 0) m_run = fp8_tile_max<NKB>(sc, ce[0]);
+        headroom(sc, ce[0]);
+        float tsum;
+        i32x8 pb;
+        fp8_probs<NKB>(sc, ce[0], m_run - (float)kP8Exp, tsum, pb);
+        l_run += tsum;
+        pv(v_cur, pb);
+      }
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+      step_s(std::integral_constant<int, 0>{}, j);
+      if (j + 1 < n_tiles) step_s(std::integral_constant<int, 1>{}, j + 1);
+    }
+  } else {
+    // prologue: K and V of tile 0 and K of tile 1
+    load_tile_rsrc<LPW>(k_tile(S, 0), smem + kK0, wave, k_off);
+    load_tile_rsrc<LPW>(v_tile(S, 0), smem + kV0, wave, v_off);
+    if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, 1), smem + kK1, wave, k_off);
+
+    f32x16 s_a[1][NKB], s_b[1][NKB];
+    float ce_a[1], ce_b[1];
+    wait_vm_lgkm0<0>();
+    workgroup_barrier();
+    if (n_act > 0) {
+      // m starts at the row max of tile 0, which holds key 0 <= every row
+      scores(kK0, s_a);
+      tile_mask<1, NKB, CAUSAL>(s_a, 0, wave_row0, S, c, l32, hi, ce_a);
+      m_run = fp8_tile_max<NKB>(s_a, ce_a[0]);
+    }
+
+    // One step for tile j (parity PAR): scores of tile j + 1 beside the
+    // probabilities of tile j, the headroom test, then P V of tile j.
+    auto step = [&](auto par, int j, f32x16 (&cur)[1][NKB], float (&ce_cur)[1],
+                    f32x16 (&nxt)[1][NKB], float (&ce_nxt)[1]) {
+      constexpr int PAR = decltype(par)::value;
+      const uint32_t k_next = PAR ? kK0 : kK1, k_free = PAR ? kK1 : kK0;
+      const uint32_t v_cur = PAR ? kV1 : kV0, v_free = PAR ? kV0 : kV1;
+      wait_vm_lgkm0<0>();
+      workgroup_barrier();
+      // K of tile j + 2 into tile j's K stage, V of tile j + 1 into tile
+      // j - 1's V stage (tiles past the last get zero-length buffers)
+      load_tile_rsrc<LPW>(k_tile(j + 2 < n_tiles ? S : 0, j + 2), smem + k_free, wave,
+                          k_off);
+      load_tile_rsrc<LPW>(v_tile(j + 1 < n_tiles ? S : 0, j + 1), smem + v_free, wave,
+                          v_off);
+      if (j < n_act) {
+        scores(k_next, nxt);
+        headroom(cur, ce_cur[0]);
+        float tsum;
+        i32x8 pb;
+        fp8_probs<NKB>(cur, ce_cur[0], m_run - (float)kP8Exp, tsum, pb);
+        l_run += tsum;
+        pv(v_cur, pb);
+        if (j + 1 < n_act) {
+          if (tile_needs_mask<1, NKB, CAUSAL>((j + 1) * Bc, wave_row0, S))
+            tile_mask<1, NKB, CAUSAL>(nxt, (j + 1) * Bc, wave_row0, S, c, l32, hi, ce_nxt);
+          else
+            ce_nxt[0] = c;
+        }
+      }
+    };
+    for (int j = 0; j < n_tiles; j += 2) {
+      step(std::integral_constant<int, 0>{}, j, s_a, ce_a, s_b, ce_b);
+      if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1, s_b, ce_b, s_a, ce_a);
+    }
   }
   wait_vm_lgkm0<0>();
 
@@ -341,7 +387,7 @@ extern "C" int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   if (B < 1 || H < 1 || S < 1 || B > 65535 || H > 65535 || S > INT32_MAX - 1024)
     return FA2_ERR_SHAPE;
   if (dtype != FA2_F16 && dtype != FA2_BF16) return FA2_ERR_DTYPE;
-  if (!(D == 64 || D == 128)) return FA2_ERR_HEADDIM;
+  if (!(D == 64 || D == 128 || D == 256)) return FA2_ERR_HEADDIM;
   // the elements within int64 (a head may span any size: tiles are
   // addressed from 64-bit starts); the grid's linear block index in 32 bits
   if (!fa2_host::elements_fit_int64(B, H, S, D)) return FA2_ERR_SHAPE;
@@ -365,9 +411,11 @@ extern "C" int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   if (dev != FA2_OK) return dev;
   (void)hipGetLastError();
   const hipError_t err =
-      D == 64 ? launch_fp8_any<64>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale, n_cu,
-                                   (hipStream_t)stream)
-              : launch_fp8_any<128>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale, n_cu,
-                                    (hipStream_t)stream);
+      D == 64    ? launch_fp8_any<64>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale, n_cu,
+                                      (hipStream_t)stream)
+      : D == 128 ? launch_fp8_any<128>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale,
+                                       n_cu, (hipStream_t)stream)
+                 : launch_fp8_any<256>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale,
+                                       n_cu, (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }

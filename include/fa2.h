@@ -323,7 +323,7 @@ int fa2_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o
  * q_descale, k_descale, v_descale  finite and > 0 (FA2_ERR_SCALE).
  * o         (B, H, S, D) contiguous, `dtype` (FA2_F16 or FA2_BF16), the
  *           output's element type only; 16-byte aligned.
- * lse, B, H, S, causal, scale, stream as for fa2_fwd; D is 64 or 128.
+ * lse, B, H, S, causal, scale, stream as for fa2_fwd; D is 64, 128 or 256.
  *
  * Arithmetic: S = Q K^T and O~ = P V on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x
  * e4m3, fp32 accumulation; the instruction's internal sum is not exact
@@ -335,7 +335,7 @@ int fa2_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o
  * on the dequantized inputs by more than fa2_fwd's does: by at most a
  * forward error bound set by the rounding of P to e4m3 (3 mantissa bits)
  * and the FP8 product's sum, which the tests evaluate per output.
- * Returns the codes of fa2_fwd (FA2_ERR_HEADDIM for D other than 64, 128).
+ * Returns the codes of fa2_fwd.
  */
 int fa2_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                 int B, int H, int S, int D, int causal, float scale, float q_descale,

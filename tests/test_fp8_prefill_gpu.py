@@ -50,7 +50,7 @@ def _check(w, seed=0, scale=None, label=""):
 SMALL_S = [1, 2, 63, 64, 65, 129, 200, 383]
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_small_shapes(D, dtype, causal):
@@ -60,7 +60,7 @@ def test_fp8_small_shapes(D, dtype, causal):
         _check(w, seed=S, label=f"S={S}")
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_fp8_peaky_and_negative_scale(D):
     for causal in (False, True):
         w = wl.Workload("fp8_peaky", 1, 3, 700, D, "bf16", causal, qk_mult=3.0)
@@ -98,6 +98,14 @@ def test_fp8_rising_scores_force_rescale():
         print(f"[fp8 parity] rising causal={causal}: max|dO|/bound {(do / bo).max():.3f}, "
               f"max|dlse|/bound {(dl / bl).max():.3f}", flush=True)
         assert (do <= bo).all() and (dl <= bl).all()
+
+
+def test_fp8_ragged_d256_every_row():
+    """B=4, H=16, S=4097, D=256, bf16 out, causal (the ragged benchmark
+    shape, on the unpipelined D = 256 loop): every output within the bound."""
+    w = wl.Workload("fp8_ragged_d256", 4, 16, 4097, 256, "bf16", True)
+    announce(f"fp8 ragged D=256 {w}")
+    _check(w, seed=0, label="ragged D=256")
 
 
 def test_fp8_headline_shape_every_row():
