@@ -534,7 +534,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   int g_t0 = t0, g_stop = t_stop, n_steps = t_stop - t0, h_split = 0;
   if constexpr (KG > 1) {
     const int n = t_stop - t0;
-    h_split = CAUSAL ? min(n / 2, q0 / Bc - t0) : n / 2;
+    h_split = CAUSAL ? max(0, min(n / 2, q0 / Bc - t0)) : n / 2;
     g_t0 = grp ? t0 + h_split : t0;
     g_stop = grp ? t_stop : t0 + h_split;
     n_steps = max(h_split, n - h_split);
