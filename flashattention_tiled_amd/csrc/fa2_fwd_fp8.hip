@@ -175,8 +175,12 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
   const int r8 = 8 * (e8 >> 2) + 4 * hi + (e8 & 3);
   const uint32_t v8_base = (uint32_t)(r8 * D + 16 * grp8 + 8 * (lane & 1));
   const uint32_t v8_x = (uint32_t)(16 * swz_v8<D>(r8));
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // The empty asm hides the constant from the optimiser, so it stays in eight
+  // registers for the whole loop instead of being rebuilt before each use
+  // (saves about 14 moves per key tile). At D = 256 no registers are spare.
+  if constexpr (!SH::kSerial) __asm__ volatile("" : "+v"(ones));
 
   f32x16 acc_o[NDB], acc_l;
 #pragma unroll
