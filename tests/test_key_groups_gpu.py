@@ -7,7 +7,8 @@ of 128 rows on the 256 units of an MI355X). The cases cover the split at
 every query tile, including the first (whose keys all go to the second
 group), ragged sequence ends inside a group's last tile, an odd number of
 key tiles (the groups run different numbers of tiles), both dtypes, a
-negative scale, strided views, and the shape beside it that keeps the main
+negative scale, strided views, grids from one to two tiles per compute unit
+(the LLM layer's among them), and the shape beside it that keeps the main
 tile. Tolerances: max |dO| <= 2e-3 (fp16) / 1.6e-2 (bf16), lse relative
 error <= 1e-4.
 """
@@ -29,6 +30,9 @@ CASES = [
     (1, 4, 8192, "f16", 1),      # 256 tiles: one long head per 64 units
     (1, 36, 960, "f16", -1),     # 288 tiles, negative scale
     (1, 16, 2049, "bf16", 1),    # 272 tiles, a one-row last tile
+    (1, 32, 2048, "f16", 1),     # 512 tiles: the LLM layer's attention
+    (1, 30, 1900, "bf16", 1),    # 450 tiles, 15 per head, ragged end
+    (2, 16, 1700, "f16", -1),    # 448 tiles, 14 per head, ragged end, negative scale
 ]
 
 
