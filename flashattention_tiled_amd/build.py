@@ -57,6 +57,21 @@ def build_probe(force: bool = True) -> str:
     return PROBE_LIB_PATH
 
 
+TIMELINE_LIB_PATH = os.path.join(PKG, "libfa2_timeline.so")
+
+
+def build_timeline(force: bool = True) -> str:
+    """Compile the library's sources with -DFA2_TIMELINE, in which every
+    prefill workgroup records clock stamps (include/fa2_timeline.h; a
+    measurement aid, read by timeline.py), into libfa2_timeline.so."""
+    if force or not os.path.exists(TIMELINE_LIB_PATH):
+        tmp = TIMELINE_LIB_PATH + ".tmp"
+        cmd = [HIPCC, *HIP_FLAGS, "-DFA2_TIMELINE", "-I", INCLUDE, "-o", tmp, *SOURCES]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, TIMELINE_LIB_PATH)
+    return TIMELINE_LIB_PATH
+
+
 # the files that hold the split-KV kernels' code (partial and combine)
 SPLITKV_KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
                           ("fa2_plan.h", "fa2_tile.h", "fa2_combine.h", "fa2_splitkv.hip")]

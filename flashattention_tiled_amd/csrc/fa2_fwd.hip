@@ -53,6 +53,28 @@ using fa2_host::rows_disjoint;
 
 namespace {
 
+// Per-workgroup timeline, a measurement aid compiled in only with
+// -DFA2_TIMELINE (into a library of its own, see timeline.py): wave 0 of
+// each of the first kTimelineWgs workgroups of a launch records the 100 MHz
+// real-time clock at its start, after its prologue's barrier (at its first
+// key tile on the unpipelined path), after its key loop and at its end; its
+// compute unit's hardware ids (HW_ID, and XCC_ID above bit 32); and its
+// query tile, (b, h) and key-loop steps. Vector stores of thread 0.
+#ifdef FA2_TIMELINE
+constexpr int kTimelineWgs = 16384, kTimelineSlots = 8;
+__device__ unsigned long long fa2_tl[kTimelineWgs * kTimelineSlots];
+#define FA2_TL(lin, slot, value)                                                  \
+  do {                                                                            \
+    if ((lin) < kTimelineWgs && threadIdx.x == 0)                                 \
+      fa2_tl[(size_t)(lin) * kTimelineSlots + (slot)] = (unsigned long long)(value); \
+  } while (0)
+#define FA2_TL_NOW() __builtin_amdgcn_s_memrealtime()
+#else
+#define FA2_TL(lin, slot, value) \
+  do {                           \
+  } while (0)
+#endif
+
 constexpr float kSumLimit = 4096.0f;  // lazy-rescale threshold on a lane's tile sum of P
 // The loads one pipeline step issues: this wave's LPW blocks of the next K
 // tile, then its LPW blocks of the next V tile, issued one at a time between
@@ -427,6 +449,9 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   const int n_bh = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   const int bh = lin % n_bh;
+  FA2_TL(lin, 0, FA2_TL_NOW());
+  FA2_TL(lin, 4, (unsigned long long)(unsigned)__builtin_amdgcn_s_getreg(0xf804) |
+                     ((unsigned long long)(unsigned)__builtin_amdgcn_s_getreg(0xf814) << 32));
   int qt, chunk = 0;
   if (ks.ct > 0) {
     split_item(lin / n_bh, ks, CAUSAL, qt, chunk);
@@ -564,6 +589,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
       load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, g_t0 + i), ring + kK0 + i * TB, gw, k_off);
       load_tile_rsrc<LPW>(v_tile(i < n_tiles ? S : 0, g_t0 + i), ring + kV0 + i * TB, gw, v_off);
     }
+    FA2_TL(lin, 1, FA2_TL_NOW());
     auto step_s = [&](auto sj_c, int j) {
       constexpr int SJ = decltype(sj_c)::value, SF = (SJ + NST - 1) % NST;
       wait_vm_lgkm0<(NST - 2) * 2 * LPW>();
@@ -616,6 +642,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     // them) before the first tile's scores
     wait_vm_lgkm0<0>();
     workgroup_barrier();
+    FA2_TL(lin, 1, FA2_TL_NOW());
     if (n_act > 0) {
       // m starts at the row max of tile g_t0, which holds an unmasked key
       // for every row (key g_t0 B_c <= q0), so m is finite from here on
@@ -703,6 +730,9 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   // the last steps' loads (zeros into free stages) must land before the
   // workgroup's LDS is released (or reused for the merge)
   wait_vm_lgkm0<0>();
+  FA2_TL(lin, 2, FA2_TL_NOW());
+  FA2_TL(lin, 5, (unsigned long long)(unsigned)qt | ((unsigned long long)(unsigned)bh << 16) |
+                     ((unsigned long long)(unsigned)n_steps << 32));
 
   if constexpr (KG > 1) {
     // Merge the key groups' partial results for each row, as the pages'
@@ -778,6 +808,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
       if (hi == 0) lse[(size_t)bh * S + row] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
+  FA2_TL(lin, 3, FA2_TL_NOW());
 }
 
 // Launch the kernel over (B, H, S); `st` gives the strides of a strided call
@@ -984,3 +1015,30 @@ extern "C" int fa2_fwd_balanced(const void* q, const void* k, const void* v, voi
   return prefill_call(q, k, v, o, lse, B, H, S, D, strides, causal, scale, dtype, true, workspace,
                       workspace_bytes, stream);
 }
+
+#ifdef FA2_TIMELINE
+// The timeline build's own entry points (include/fa2_timeline.h).
+namespace {
+__global__ void fa2_timeline_clear_kernel() {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (size_t)kTimelineWgs * kTimelineSlots) fa2_tl[i] = 0ull;
+}
+}  // namespace
+
+extern "C" int fa2_timeline_capacity(void) { return kTimelineWgs; }
+
+extern "C" int fa2_timeline_clear(void* stream) {
+  fa2_timeline_clear_kernel<<<kTimelineWgs * kTimelineSlots / 256, 256, 0, (hipStream_t)stream>>>();
+  return hipGetLastError() == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
+}
+
+extern "C" int fa2_timeline_read(unsigned long long* host, int n_wg) {
+  if (!host || n_wg < 0 || n_wg > kTimelineWgs) return FA2_ERR_SHAPE;
+  if (hipDeviceSynchronize() != hipSuccess) return FA2_ERR_LAUNCH;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(fa2_tl),
+                             (size_t)n_wg * kTimelineSlots * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess
+             ? FA2_OK
+             : FA2_ERR_LAUNCH;
+}
+#endif

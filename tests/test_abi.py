@@ -550,7 +550,7 @@ PROBE_HEADER = os.path.join(ROOT, "include", "fa2_probe.h")
 
 def test_every_header_has_its_library():
     headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
-    assert headers == ["fa2.h", "fa2_probe.h"]
+    assert headers == ["fa2.h", "fa2_probe.h", "fa2_timeline.h"]
 
 
 @pytest.fixture(scope="module")
@@ -615,3 +615,45 @@ def test_probe_flops_and_validation(probe):
     assert probe.fa2_probe_mfma_ceiling(fake, 1, 0, fake, fake, 1, None) == 2
     assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, fake, 2, None) == 4
     assert probe.fa2_probe_mfma_ceiling(fake, 1, 1, fake, fake, -1, None) == 4
+
+
+# ---------------------------------------------------------------------------
+# the timeline build (include/fa2_timeline.h, libfa2_timeline.so): the same
+# sources with per-workgroup clock stamps, a measurement aid of its own library
+# ---------------------------------------------------------------------------
+TIMELINE_HEADER = os.path.join(ROOT, "include", "fa2_timeline.h")
+
+
+@pytest.fixture(scope="module")
+def timeline():
+    from flashattention_tiled_amd.build import TIMELINE_LIB_PATH, build_timeline
+
+    if not os.path.exists(TIMELINE_LIB_PATH):
+        build_timeline(force=False)
+    import torch  # noqa: F401  (shares torch's HIP runtime)
+
+    t = ctypes.CDLL(TIMELINE_LIB_PATH)
+    t.fa2_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    return t
+
+
+def test_timeline_exports_the_library_and_its_header(timeline):
+    from flashattention_tiled_amd.build import TIMELINE_LIB_PATH
+
+    text = open(TIMELINE_HEADER).read()
+    declared = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa2_\w+)\s*\(", text, flags=re.M)
+    assert sorted(declared) == ["fa2_timeline_capacity", "fa2_timeline_clear", "fa2_timeline_read"]
+    _, defined = _elf_dynamic(TIMELINE_LIB_PATH)
+    assert sorted(n for n in defined if n.startswith("fa2")) == sorted(declared + _declared_functions())
+    # the product library records nothing and exports none of it
+    _, product = _elf_dynamic(fa.LIB_PATH)
+    assert not [n for n in product if "timeline" in n]
+
+
+def test_timeline_read_validates_before_touching_the_device(timeline):
+    cap = timeline.fa2_timeline_capacity()
+    assert cap == 16384
+    buf = (ctypes.c_ulonglong * 8)()
+    assert timeline.fa2_timeline_read(None, 1) == fa.FA2_ERR_SHAPE
+    assert timeline.fa2_timeline_read(ctypes.addressof(buf), -1) == fa.FA2_ERR_SHAPE
+    assert timeline.fa2_timeline_read(ctypes.addressof(buf), cap + 1) == fa.FA2_ERR_SHAPE
