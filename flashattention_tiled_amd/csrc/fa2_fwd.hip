@@ -410,7 +410,6 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int S, float c /* scale * log2(e) */, int pair_split, Strides st, KeySplit ks) {
   using SH = Shape<D, ALT>;
-  using E = Elem<DT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
   constexpr int CPR = SH::kChunksPerRow, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
   constexpr int NKB = Bc / 32;  // 32-key blocks per tile
@@ -737,38 +736,69 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   if constexpr (KG > 1) {
     // Merge the key groups' partial results for each row, as the pages'
     // split of a row's keys into parts merges them: both are rescaled to the
-    // larger reference max, O~ and both sums added. Group 1 stores its O~,
-    // m, l and l' in the LDS the rings leave free, lane by lane (lane l of
-    // wave w of either group holds the same elements); group 0 combines them
-    // with its own (or takes them over when it had no tiles) and writes the
-    // rows.
+    // larger reference max, O~ and both sums added. Each group finishes half
+    // of every row's columns, group 0 the first NDB / 2 column blocks and
+    // group 1 the rest: it hands the other half of its O~, with its m, l and
+    // l', to the other group through the LDS the rings leave free (lane l of
+    // wave w of either group holds the same elements) and takes that group's
+    // half in turn. Group 0 has no tiles (weight 0 for its unset state) when
+    // h_split is 0. A key split never takes this tile: one chunk.
+    constexpr int NH = NDB / 2, HF = SH::kMergeFloats;
+    static_assert(NDB % 2 == 0 && HF == NH * 16 + 3 && 2 * GW * HF * 64 * 4 <= SH::kLdsBytes,
+                  "merge area");
     workgroup_barrier();
-    float* mg = (float*)smem + (size_t)gw * SH::kMergeFloats * 64 + lane;
-    if (grp == 1) {
+    float* const give = (float*)smem + (size_t)(grp * GW + gw) * HF * 64 + lane;
+    const float* const take = (const float*)smem + (size_t)((1 - grp) * GW + gw) * HF * 64 + lane;
+    auto hand = [&](auto first) {
+      constexpr int F = decltype(first)::value;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int i = 0; i < NH; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mg[(db * 16 + r) * 64] = acc_o[0][db][r];
-      mg[(NDB * 16) * 64] = m_run[0];
-      mg[(NDB * 16 + 1) * 64] = l_run[0];
-      mg[(NDB * 16 + 2) * 64] = l_rnd[0];
-    }
+        for (int r = 0; r < 16; ++r) give[(i * 16 + r) * 64] = acc_o[0][F + i][r];
+    };
+    if (grp == 0)
+      hand(std::integral_constant<int, NH>{});
+    else
+      hand(std::integral_constant<int, 0>{});
+    give[(NH * 16) * 64] = m_run[0];
+    give[(NH * 16 + 1) * 64] = l_run[0];
+    give[(NH * 16 + 2) * 64] = l_rnd[0];
     workgroup_barrier();
-    if (grp == 1) return;
-    const float m1 = mg[(NDB * 16) * 64];
-    const float l1 = mg[(NDB * 16 + 1) * 64], lr1 = mg[(NDB * 16 + 2) * 64];
-    // group 0 without tiles: weight 0 for its (unset) state
-    const float m_new = h_split > 0 ? fmaxf(m_run[0], m1) : m1;
-    const float a0 = h_split > 0 ? __builtin_amdgcn_exp2f(m_run[0] - m_new) : 0.f;
+    const float m_t = take[(NH * 16) * 64];
+    const float l_t = take[(NH * 16 + 1) * 64], lr_t = take[(NH * 16 + 2) * 64];
+    const bool g0 = grp == 0;
+    const float m0 = g0 ? m_run[0] : m_t, m1 = g0 ? m_t : m_run[0];
+    const float m_new = h_split > 0 ? fmaxf(m0, m1) : m1;
+    const float a0 = h_split > 0 ? __builtin_amdgcn_exp2f(m0 - m_new) : 0.f;
     const float a1 = __builtin_amdgcn_exp2f(m1 - m_new);
+    const float l_tot = xor32_sum(g0 ? l_run[0] * a0 + l_t * a1 : l_t * a0 + l_run[0] * a1);
+    const float l_o = xor32_sum(g0 ? l_rnd[0] * a0 + lr_t * a1 : lr_t * a0 + l_rnd[0] * a1);
+    const int row = wave_row0 + l32;
+    if (row < S) {
+      const float inv = 1.0f / l_o;
+      // this group's half: blocks F .. F + NH - 1, the other group's
+      // values from LDS; x0 * a0 + x1 * a1 with x0 group 0's value
+      auto finish = [&](auto first) {
+        constexpr int F = decltype(first)::value;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int i = 0; i < NH; ++i) {
+          float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        acc_o[0][db][r] = acc_o[0][db][r] * a0 + mg[(db * 16 + r) * 64] * a1;
-    m_run[0] = m_new;
-    l_run[0] = l_run[0] * a0 + l1 * a1;
-    l_rnd[0] = l_rnd[0] * a0 + lr1 * a1;
+          for (int r = 0; r < 16; ++r) {
+            const float own = acc_o[0][F + i][r], other = take[(i * 16 + r) * 64];
+            x[r] = F == 0 ? own * a0 + other * a1 : other * a0 + own * a1;
+          }
+          store_o_block<DT>(o + o_at + (size_t)row * o_rs + 32 * (F + i), x, inv, hi);
+        }
+      };
+      if (g0)
+        finish(std::integral_constant<int, 0>{});
+      else
+        finish(std::integral_constant<int, NH>{});
+      if (g0 && hi == 0) lse[(size_t)bh * S + row] = (m_new + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    FA2_TL(lin, 3, FA2_TL_NOW());
+    return;
   }
 
   // Epilogue: O = O~ / sum(rounded P), rounded once to the input dtype, and
@@ -799,12 +829,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
       const float inv = 1.0f / l_o;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 out = {E::pack2(acc_o[rb][db][4 * g] * inv, acc_o[rb][db][4 * g + 1] * inv),
-                             E::pack2(acc_o[rb][db][4 * g + 2] * inv, acc_o[rb][db][4 * g + 3] * inv)};
-          *(u32x2*)(o + o_at + (size_t)row * o_rs + 32 * db + 8 * g + 4 * hi) = out;
-        }
+        store_o_block<DT>(o + o_at + (size_t)row * o_rs + 32 * db, acc_o[rb][db], inv, hi);
       if (hi == 0) lse[(size_t)bh * S + row] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }

@@ -112,7 +112,6 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
     const unsigned char* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
     float c /* scale * log2(e) * q_descale * k_descale */, float v_mult, int pair_split) {
   using SH = Fp8Shape<D>;
-  using E = Elem<DT>;
   constexpr int Br = SH::kBr, Bc = SH::kBc, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
   constexpr int NKB = Bc / 32, NKS = SH::kKSteps, NDB = D / 32;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SH::kLdsBytes];
@@ -342,12 +341,7 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
     const float inv = v_mult / acc_l[0];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 out = {E::pack2(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
-                           E::pack2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv)};
-        *(u32x2*)(o + head + (size_t)row * D + 32 * db + 8 * g + 4 * hi) = out;
-      }
+      store_o_block<DT>(o + head + (size_t)row * D + 32 * db, acc_o[db], inv, hi);
     if (hi == 0)
       lse[(size_t)bh * S + row] =
           (m_run + __builtin_amdgcn_logf(l_tot) - (float)kP8Exp) * kLn2;

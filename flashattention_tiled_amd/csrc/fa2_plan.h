@@ -103,10 +103,12 @@ template <int D, bool ALT = false> struct Shape {
   static constexpr int kStages = Tile<D, ALT>::kStages;
   static constexpr bool kPipelined = Tile<D, ALT>::kPipelined != 0;
   static constexpr int kRingBytes = 2 * kStages * kTileBytes;  // one group's K ring + V ring
-  // the merge of the key groups: a group's O~ (D / 2 floats per lane) and
-  // its m, l and l' per lane, for each of its waves, laid out lane-major
-  static constexpr int kMergeFloats = D / 2 + 3;
-  static constexpr int kMergeBytes = kKeyGroups > 1 ? kGroupWaves * kMergeFloats * 64 * 4 : 0;
+  // the merge of the key groups: per wave and group, the half of its O~
+  // the other group finishes (D / 4 floats per lane) and its m, l and l'
+  // per lane, laid out lane-major
+  static constexpr int kMergeFloats = D / 4 + 3;
+  static constexpr int kMergeBytes =
+      kKeyGroups > 1 ? kKeyGroups * kGroupWaves * kMergeFloats * 64 * 4 : 0;
   static constexpr int kLdsBytes =
       kKeyGroups * kRingBytes > kMergeBytes ? kKeyGroups * kRingBytes : kMergeBytes;
   static_assert(kWaves % kKeyGroups == 0 && kKeyGroups <= 2, "key groups");

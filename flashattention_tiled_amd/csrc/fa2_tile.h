@@ -177,6 +177,29 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Write one 32-column block of a row of O, x * inv rounded to the dtype,
+// from the accumulator layout of O~^T: lane (l32, hi) holds columns
+// 8 g + 4 hi + 0..3 of its row in x[4 g .. 4 g + 3], g = 0..3. One swap of
+// the upper half's even-g and the lower half's odd-g words gives lane hi the
+// 8 consecutive columns 16 gp + 8 hi + 0..7 of each pair gp of g: two
+// 16-byte stores per lane, each writing 32 contiguous bytes of every row.
+// `dst` points at the block's first column of this lane's row (16-byte
+// aligned). X is f32x16 or float[16].
+template <int DT, class X>
+__device__ __forceinline__ void store_o_block(uint16_t* dst, const X& x, float inv, int hi) {
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+    const int r = 8 * gp;
+    const uint32_t e0 = Elem<DT>::pack2(x[r] * inv, x[r + 1] * inv);
+    const uint32_t e1 = Elem<DT>::pack2(x[r + 2] * inv, x[r + 3] * inv);
+    const uint32_t d0 = Elem<DT>::pack2(x[r + 4] * inv, x[r + 5] * inv);
+    const uint32_t d1 = Elem<DT>::pack2(x[r + 6] * inv, x[r + 7] * inv);
+    const auto y0 = __builtin_amdgcn_permlane32_swap(e0, d0, false, false);
+    const auto y1 = __builtin_amdgcn_permlane32_swap(e1, d1, false, false);
+    *(u32x4*)(dst + 16 * gp + 8 * hi) = u32x4{y0[0], y1[0], y0[1], y1[1]};
+  }
+}
+
 // Per-lane byte offsets, within one tile, of the 16-byte chunks this wave
 // loads: LDS slot p = block * 64 + lane of the tile receives chunk
 // (p % CPR) ^ swz(row) of key row p / CPR.
