@@ -619,6 +619,9 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     }
     static_assert(NST <= 4, "unroll");
   } else {
+    // Q's loads stay ahead of the tile loads, so that the wait below for the
+    // first K tile covers them while V of tile 0 and K of tile 1 still land
+    __builtin_amdgcn_sched_barrier(0);
     load_tile_rsrc<LPW>(k_tile(n_tiles > 0 ? S : 0, g_t0), ring + kK0, gw, k_off);
     if constexpr (NST == 2) {
       load_tile_rsrc<LPW>(v_tile(n_tiles > 0 ? S : 0, g_t0), ring + kV0, gw, v_off);
@@ -637,9 +640,16 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
 
     f32x16 s_a[RB][NKB], s_b[RB][NKB];
     float ce_a[RB], ce_b[RB];
-    // all of them (and the Q loads, which the compiler may have issued after
-    // them) before the first tile's scores
-    wait_vm_lgkm0<0>();
+    // Q and K of the first tile before its scores; the rest of the
+    // prologue's loads are waited for at the top of the first step
+    if constexpr (NST == 2) {
+      if (n_tiles > 1)
+        wait_vm_lgkm0<2 * LPW>();
+      else
+        wait_vm_lgkm0<LPW>();
+    } else {
+      wait_vm_lgkm0<2 * (NST - 1) * LPW>();
+    }
     workgroup_barrier();
     FA2_TL(lin, 1, FA2_TL_NOW());
     if (n_act > 0) {
