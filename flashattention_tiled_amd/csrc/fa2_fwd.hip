@@ -485,15 +485,20 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     k_rb = v_rb = 2u * D;
   }
 
-  // Q^T operands: lane holds Q[row][16 s + 8 hi .. +7] of each of its rows.
+  // Q^T operands: lane holds Q[row][16 s + 8 hi .. +7] of each of its rows,
+  // loaded here or (SH::kQStaged) through LDS in the prologue, in whole
+  // 1 KiB blocks and, with key groups, once for both groups.
+  constexpr bool QS = SH::kQStaged;
   u32x4 qf[RB][NDS];
+  if constexpr (!QS) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = wave_row0 + 32 * rb + l32;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = wave_row0 + 32 * rb + l32;
 #pragma unroll
-    for (int s = 0; s < NDS; ++s) {
-      qf[rb][s] = u32x4{0, 0, 0, 0};
-      if (row < S) qf[rb][s] = *(const u32x4*)(q + q_at + (size_t)row * q_rs + 16 * s + 8 * hi);
+      for (int s = 0; s < NDS; ++s) {
+        qf[rb][s] = u32x4{0, 0, 0, 0};
+        if (row < S) qf[rb][s] = *(const u32x4*)(q + q_at + (size_t)row * q_rs + 16 * s + 8 * hi);
+      }
     }
   }
 
@@ -622,6 +627,28 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     // Q's loads stay ahead of the tile loads, so that the wait below for the
     // first K tile covers them while V of tile 0 and K of tile 1 still land
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (QS) {
+      // Q rows Bc h .. Bc h + Bc - 1 of the tile (half h) in K's LDS layout:
+      // with key groups group g loads half g into the second stage of its V
+      // ring, else every wave loads its share of both halves, half 1 into
+      // the region after the ring. The first step refills that V stage only
+      // after every wave has read Q (its top barrier).
+      const uint32_t q_rb = (uint32_t)q_rs * 2u;
+      const unsigned char* q_head = (const unsigned char*)(q + q_at);
+      uint32_t q_off[LPW];
+      if constexpr (STRIDED)
+        tile_load_offsets_strided<D, LPW, false>(gw, lane, q_rb, q_off);
+      else
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) q_off[i] = k_off[i];
+      auto q_half = [&](int h) { return tile_rsrc_rows(q_head, S, q0 + Bc * h, q_rb, rows_within_2g(q_rb)); };
+      if constexpr (KG > 1) {
+        load_tile_rsrc<LPW>(q_half(grp), ring + kV1, gw, q_off);
+      } else {
+        load_tile_rsrc<LPW>(q_half(0), smem + kV1, gw, q_off);
+        load_tile_rsrc<LPW>(q_half(1), smem + SH::kRingBytes, gw, q_off);
+      }
+    }
     load_tile_rsrc<LPW>(k_tile(n_tiles > 0 ? S : 0, g_t0), ring + kK0, gw, k_off);
     if constexpr (NST == 2) {
       load_tile_rsrc<LPW>(v_tile(n_tiles > 0 ? S : 0, g_t0), ring + kV0, gw, v_off);
@@ -651,6 +678,14 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
       wait_vm_lgkm0<2 * (NST - 1) * LPW>();
     }
     workgroup_barrier();
+    if constexpr (QS) {
+      // this wave's rows: rows 32 (gw % 2) .. + 31 of half gw / 2
+      const uint32_t q_half_at = KG > 1 ? (uint32_t)((gw / 2) * SH::kRingBytes) + kV1
+                                        : (gw / 2 == 0 ? kV1 : (uint32_t)SH::kRingBytes);
+      const uint32_t q_base = q_half_at + k_lane + (uint32_t)((gw % 2) * 32 * CPR * 16);
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) qf[0][s] = *(const u32x4*)(smem + (q_base ^ (uint32_t)(32 * s)));
+    }
     FA2_TL(lin, 1, FA2_TL_NOW());
     if (n_act > 0) {
       // m starts at the row max of tile g_t0, which holds an unmasked key
@@ -966,11 +1001,11 @@ int prefill_call(const void* q, const void* k, const void* v, void* o, float* ls
     st = Strides{strides[0], strides[1], strides[2],  strides[3], strides[4],  strides[5],
                  strides[6], strides[7], strides[8],  strides[9], strides[10], strides[11]};
   }
-  // the elements of every tensor within int64, and the 256 rows of K or V
-  // one tile load spans within 31-bit offsets from the tile's start (buffer
-  // loads; a head itself may span any size)
-  if (!elements_fit_int64(B, H, S, D) || 256LL * st.ks * 2 > (long long)INT32_MAX ||
-      256LL * st.vs * 2 > (long long)INT32_MAX)
+  // the elements of every tensor within int64, and the 256 rows of Q, K or
+  // V one tile load spans within 31-bit offsets from the tile's start
+  // (buffer loads; a head itself may span any size)
+  if (!elements_fit_int64(B, H, S, D) || 256LL * st.qs * 2 > (long long)INT32_MAX ||
+      256LL * st.ks * 2 > (long long)INT32_MAX || 256LL * st.vs * 2 > (long long)INT32_MAX)
     return FA2_ERR_SHAPE;
   // the kernel linearises its block index in a 32-bit int (a key split
   // only runs on grids of a few thousand workgroups)

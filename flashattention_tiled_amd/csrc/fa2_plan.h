@@ -109,8 +109,16 @@ template <int D, bool ALT = false> struct Shape {
   static constexpr int kMergeFloats = D / 4 + 3;
   static constexpr int kMergeBytes =
       kKeyGroups > 1 ? kKeyGroups * kGroupWaves * kMergeFloats * 64 * 4 : 0;
-  static constexpr int kLdsBytes =
-      kKeyGroups * kRingBytes > kMergeBytes ? kKeyGroups * kRingBytes : kMergeBytes;
+  // Q reaches the registers through LDS in the prologue when the query tile
+  // is two key tiles of rows (32 rows per wave, two-stage pipelined rings):
+  // its first half in the second stage of a V ring, which the prologue
+  // leaves free, its second in the other group's (with key groups) or in a
+  // region after the ring
+  static constexpr bool kQStaged = kPipelined && kStages == 2 && kRB == 1 && kBr == 2 * kBc;
+  static constexpr int kQExtraBytes = kQStaged && kKeyGroups == 1 ? kTileBytes : 0;
+  static constexpr int kLdsBytes = kKeyGroups * kRingBytes + kQExtraBytes > kMergeBytes
+                                       ? kKeyGroups * kRingBytes + kQExtraBytes
+                                       : kMergeBytes;
   static_assert(kWaves % kKeyGroups == 0 && kKeyGroups <= 2, "key groups");
   static_assert(kTileBytes % (1024 * kGroupWaves) == 0, "tile must split into 1 KiB wave loads");
   static_assert(kStages >= 2 && (kStages - 2) * 2 * kLoadsPerWave < 64, "ring depth");

@@ -47,7 +47,7 @@ typedef enum {
     FA2_ERR_NULL = 1,      /* a tensor pointer is NULL */
     FA2_ERR_SHAPE = 2,     /* B, H or S < 1, H or B > 65535, B*H*S*D elements (or their
                               bytes) overflow int64, the grid passes 2^31 workgroups, or
-                              (strided) 256 rows of K or V span 2^31 bytes or more */
+                              (strided) 256 rows of Q, K or V span 2^31 bytes or more */
     FA2_ERR_HEADDIM = 3,   /* D is not 64, 128 or 256 */
     FA2_ERR_DTYPE = 4,     /* dtype is not FA2_F16 or FA2_BF16 */
     FA2_ERR_ALIGN = 5,     /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
@@ -116,8 +116,8 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * lse      contiguous (B, H, S) floats, as for fa2_fwd.
  * Other arguments, the result and the arithmetic are those of fa2_fwd, and
  * for contiguous strides the result is bit-identical to it. A head may
- * span any size, but 256 rows of K and of V must span under 2^31 bytes
- * (256 * sequence stride * 2), the reach of one tile load's offsets.
+ * span any size, but 256 rows of Q, of K and of V must span under 2^31
+ * bytes (256 * sequence stride * 2), the reach of one tile load's offsets.
  * Overlap is judged on the byte range each tensor spans, so o and lse must
  * not fall within q's, k's or v's span. Returns FA2_ERR_STRIDE for bad
  * strides, otherwise the codes of fa2_fwd.

@@ -263,6 +263,8 @@ _STRIDED_CASES = [
     (dict(strides=_with(_CONTIG, s9=0)), fa.FA2_ERR_STRIDE),           # o batch broadcast
     (dict(strides=_with(_CONTIG, s11=64 + 8, s10=100 * 64)), fa.FA2_ERR_STRIDE),  # rows spill into next head
     (dict(strides=_with(_CONTIG, s5=1 << 23)), fa.FA2_ERR_SHAPE),      # 256 K rows span 2^32 B
+    (dict(strides=_with(_CONTIG, s2=1 << 23)), fa.FA2_ERR_SHAPE),      # 256 Q rows span 2^32 B
+    (dict(strides=_with(_CONTIG, s8=1 << 22)), fa.FA2_ERR_SHAPE),      # 256 V rows span 2^31 B
     (dict(k=SK + 8), fa.FA2_ERR_ALIGN),
     (dict(lse=SL + 2), fa.FA2_ERR_ALIGN),
     (dict(scale=float("inf")), fa.FA2_ERR_SCALE),
