@@ -64,7 +64,10 @@ template <int D> struct Fp8Shape {
   static constexpr bool kSerial = D == 256;
   static constexpr int kTileBytes = kBc * D;  // one K or V tile of codes
   static constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;
-  static constexpr int kLdsBytes = 4 * kTileBytes;  // K and V rings, two stages each
+  // K and V rings, two stages each; with the pipelined loop also a region
+  // for the second half of Q (loaded through LDS in the prologue: its first
+  // half goes to V's second stage, which the prologue leaves free)
+  static constexpr int kLdsBytes = (kSerial ? 4 : 5) * kTileBytes;
   static constexpr int kKSteps = D / 64;            // products per 32-key block of S^T
   static_assert(kLoadsPerWave >= 1 && kTileBytes % (1024 * kWaves) == 0, "wave loads");
 };
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
   const int q_sign = c < 0.f ? (int)0x80808080 : 0;
   c = fabsf(c);
   i32x8 qf[NKS];
-  {
+  if constexpr (SH::kSerial) {
     const int row = wave_row0 + l32;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -279,15 +282,37 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
       if (j + 1 < n_tiles) step_s(std::integral_constant<int, 1>{}, j + 1);
     }
   } else {
-    // prologue: K and V of tile 0 and K of tile 1
+    // prologue: Q in whole 1 KiB blocks through LDS (rows Bc h .. Bc h +
+    // Bc - 1 in K's layout: half 0 into V's second stage, which the first
+    // step refills after every wave has read it, half 1 into the region
+    // after the rings), K and V of tile 0 and K of tile 1; then Q and K of
+    // tile 0 before the first scores
+    static_assert(Br == 2 * Bc, "Q is two key tiles of rows");
+    const unsigned char* q_head = q + head;
+    load_tile_rsrc<LPW>(tile_rsrc_rows(q_head, S, q0, D, kv_cap), smem + kV1, wave, k_off);
+    load_tile_rsrc<LPW>(tile_rsrc_rows(q_head, S, q0 + Bc, D, kv_cap), smem + 4 * TB, wave, k_off);
     load_tile_rsrc<LPW>(k_tile(S, 0), smem + kK0, wave, k_off);
     load_tile_rsrc<LPW>(v_tile(S, 0), smem + kV0, wave, v_off);
     if (n_tiles > 1) load_tile_rsrc<LPW>(k_tile(S, 1), smem + kK1, wave, k_off);
 
     f32x16 s_a[1][NKB], s_b[1][NKB];
     float ce_a[1], ce_b[1];
-    wait_vm_lgkm0<0>();
+    if (n_tiles > 1)
+      wait_vm_lgkm0<2 * LPW>();
+    else
+      wait_vm_lgkm0<LPW>();
     workgroup_barrier();
+    {
+      // this wave's rows: rows 32 (wave % 2) .. + 31 of half wave / 2
+      const unsigned char* qb = smem + (wave / 2 == 0 ? kV1 : 4 * TB) + (wave % 2) * 32 * D;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const u32x4 lo = *(const u32x4*)(qb + k_rd[s][0]);
+        const u32x4 up = *(const u32x4*)(qb + k_rd[s][1]);
+        qf[s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)up[0], (int)up[1], (int)up[2], (int)up[3]} ^ q_sign;
+      }
+    }
     if (n_act > 0) {
       // m starts at the row max of tile 0, which holds key 0 <= every row
       scores(kK0, s_a);
