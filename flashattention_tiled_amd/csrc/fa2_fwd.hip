@@ -486,11 +486,12 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   }
 
   // Q^T operands: lane holds Q[row][16 s + 8 hi .. +7] of each of its rows,
-  // loaded here or (SH::kQStaged) through LDS in the prologue, in whole
-  // 1 KiB blocks and, with key groups, once for both groups.
-  constexpr bool QS = SH::kQStaged;
+  // loaded here or through LDS in the prologue (SH::kQStaged,
+  // SH::kQThroughRing), in whole 1 KiB blocks and, with key groups, once for
+  // both groups.
+  constexpr bool QS = SH::kQStaged, QS4 = SH::kQThroughRing;
   u32x4 qf[RB][NDS];
-  if constexpr (!QS) {
+  if constexpr (!QS && !QS4) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = wave_row0 + 32 * rb + l32;
@@ -588,6 +589,30 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     // Unpipelined: iteration j computes tile j from stage j % NST, after
     // every load of iteration j - NST + 1 (tile j) has landed and every wave
     // is done with iteration j - 1, whose stage then takes tile j + NST - 1.
+    if constexpr (QS4) {
+      // Q's rows 32 i .. 32 i + 31 in K's layout in stage region i (K0, K1,
+      // V0, V1), whole 1 KiB blocks; wave w reads region w, then the rings
+      // take their first tiles
+      const uint32_t q_rb = (uint32_t)q_rs * 2u;
+      const unsigned char* q_head = (const unsigned char*)(q + q_at);
+      uint32_t q_off[LPW];
+      if constexpr (STRIDED)
+        tile_load_offsets_strided<D, LPW, false>(gw, lane, q_rb, q_off);
+      else
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) q_off[i] = k_off[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        load_tile_rsrc<LPW>(tile_rsrc_rows(q_head, S, q0 + Bc * i, q_rb, rows_within_2g(q_rb)),
+                            ring + i * TB, gw, q_off);
+      wait_vm_lgkm0<0>();
+      workgroup_barrier();
+      const uint32_t q_base = (uint32_t)(gw * TB) + k_lane;
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) qf[0][s] = *(const u32x4*)(smem + (q_base ^ (uint32_t)(32 * s)));
+      wait_vm_lgkm0<0>();
+      workgroup_barrier();
+    }
 #pragma unroll
     for (int i = 0; i + 1 < NST; ++i) {
       load_tile_rsrc<LPW>(k_tile(i < n_tiles ? S : 0, g_t0 + i), ring + kK0 + i * TB, gw, k_off);

@@ -116,6 +116,9 @@ template <int D, bool ALT = false> struct Shape {
   // region after the ring
   static constexpr bool kQStaged = kPipelined && kStages == 2 && kRB == 1 && kBr == 2 * kBc;
   static constexpr int kQExtraBytes = kQStaged && kKeyGroups == 1 ? kTileBytes : 0;
+  // Unpipelined two-stage tiles whose query tile is the four ring stages'
+  // rows (D = 256) load Q through the ring before its first key tiles.
+  static constexpr bool kQThroughRing = !kPipelined && kStages == 2 && kRB == 1 && kBr == 4 * kBc;
   static constexpr int kLdsBytes = kKeyGroups * kRingBytes + kQExtraBytes > kMergeBytes
                                        ? kKeyGroups * kRingBytes + kQExtraBytes
                                        : kMergeBytes;
