@@ -520,6 +520,20 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   // whose loads return zero)
   auto k_tile = [&](int rows, int t) { return tile_rsrc_rows(k_head, rows, t * Bc, k_rb, k_cap); };
   auto v_tile = [&](int rows, int t) { return tile_rsrc_rows(v_head, rows, t * Bc, v_rb, v_cap); };
+  // Q through LDS: a key tile's worth of Q rows from row r (rows >= S read
+  // as zero), loaded in K's LDS layout with offsets for Q's row stride
+  const uint32_t q_rb = (uint32_t)q_rs * 2u;
+  [[maybe_unused]] uint32_t q_off[LPW];
+  if constexpr (QS || QS4) {
+    if constexpr (STRIDED)
+      tile_load_offsets_strided<D, LPW, false>(gw, lane, q_rb, q_off);
+    else
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) q_off[i] = k_off[i];
+  }
+  [[maybe_unused]] auto q_rows = [&](int r) {
+    return tile_rsrc_rows((const unsigned char*)(q + q_at), S, r, q_rb, rows_within_2g(q_rb));
+  };
 
   // LDS read offsets that do not depend on the tile.
   // K^T operand: row 32 kb + l32, chunk (2 s + hi) ^ swz_k(l32).
@@ -593,18 +607,8 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
       // Q's rows 32 i .. 32 i + 31 in K's layout in stage region i (K0, K1,
       // V0, V1), whole 1 KiB blocks; wave w reads region w, then the rings
       // take their first tiles
-      const uint32_t q_rb = (uint32_t)q_rs * 2u;
-      const unsigned char* q_head = (const unsigned char*)(q + q_at);
-      uint32_t q_off[LPW];
-      if constexpr (STRIDED)
-        tile_load_offsets_strided<D, LPW, false>(gw, lane, q_rb, q_off);
-      else
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) q_off[i] = k_off[i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        load_tile_rsrc<LPW>(tile_rsrc_rows(q_head, S, q0 + Bc * i, q_rb, rows_within_2g(q_rb)),
-                            ring + i * TB, gw, q_off);
+      for (int i = 0; i < 4; ++i) load_tile_rsrc<LPW>(q_rows(q0 + Bc * i), ring + i * TB, gw, q_off);
       wait_vm_lgkm0<0>();
       workgroup_barrier();
       const uint32_t q_base = (uint32_t)(gw * TB) + k_lane;
@@ -658,20 +662,11 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
       // ring, else every wave loads its share of both halves, half 1 into
       // the region after the ring. The first step refills that V stage only
       // after every wave has read Q (its top barrier).
-      const uint32_t q_rb = (uint32_t)q_rs * 2u;
-      const unsigned char* q_head = (const unsigned char*)(q + q_at);
-      uint32_t q_off[LPW];
-      if constexpr (STRIDED)
-        tile_load_offsets_strided<D, LPW, false>(gw, lane, q_rb, q_off);
-      else
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) q_off[i] = k_off[i];
-      auto q_half = [&](int h) { return tile_rsrc_rows(q_head, S, q0 + Bc * h, q_rb, rows_within_2g(q_rb)); };
       if constexpr (KG > 1) {
-        load_tile_rsrc<LPW>(q_half(grp), ring + kV1, gw, q_off);
+        load_tile_rsrc<LPW>(q_rows(q0 + Bc * grp), ring + kV1, gw, q_off);
       } else {
-        load_tile_rsrc<LPW>(q_half(0), smem + kV1, gw, q_off);
-        load_tile_rsrc<LPW>(q_half(1), smem + SH::kRingBytes, gw, q_off);
+        load_tile_rsrc<LPW>(q_rows(q0), smem + kV1, gw, q_off);
+        load_tile_rsrc<LPW>(q_rows(q0 + Bc), smem + SH::kRingBytes, gw, q_off);
       }
     }
     load_tile_rsrc<LPW>(k_tile(n_tiles > 0 ? S : 0, g_t0), ring + kK0, gw, k_off);
