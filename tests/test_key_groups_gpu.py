@@ -51,6 +51,25 @@ def test_key_groups_every_row(case):
     assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, dt, f"key groups {case}")
 
 
+def test_key_groups_q_rows_apart_from_kv():
+    """Q as a (B, S, H, D) view (rows H * D apart) beside K and V whose rows
+    are padded to D + 64: Q's half tiles go through LDS with Q's own stride."""
+    B, H, S, D = 1, 40, 1000, 128
+    announce(f"key groups Q stride apart B={B} H={H} S={S}")
+    w = wl.Workload("key_groups_mixed", B, H, S, D, "bf16", True)
+    q, k, v = wl.make_qkv(w, seed=9)
+    q_view = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+    kv = []
+    for x in (k, v):
+        buf = torch.full((B, H, S, D + 64), float("nan"), dtype=x.dtype)
+        buf[..., :D] = x
+        kv.append(buf.to(DEV)[..., :D])
+    o, lse = fa.attention(q_view, kv[0], kv[1], causal=True, scale=w.scale, balanced=False)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_full(q, k, v, True, w.scale)
+    assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, "bf16", "key groups Q stride apart")
+
+
 def test_key_groups_strided():
     """Q, K and V as views into one packed (B, S, 3, H, D) projection."""
     B, H, S, D = 1, 48, 700, 128

@@ -4,7 +4,10 @@ the oracle, and nothing written outside o's rows.
 
 Layouts: (B, S, H, D) views (a transposed projection output), the three
 views of one packed (B, S, 3, H, D) QKV buffer, a K and V of one head shared
-by all heads (head stride 0), and rows padded to D + 64 elements.
+by all heads (head stride 0), rows padded to D + 64 elements, and Q's rows
+apart by another stride than K's and V's (a (B, S, H, D) view of Q beside
+K and V with padded rows), so that no stride of one tensor stands in for
+another's.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ from gpu_helpers import DEV, announce, assert_parity, oracle_full, oracle_rows, 
 
 pytestmark = pytest.mark.gpu
 
-LAYOUTS = ["bshd", "packed_qkv", "kv_broadcast", "padded"]
+LAYOUTS = ["bshd", "packed_qkv", "kv_broadcast", "padded", "mixed"]
 
 
 def _strided(layout, q, k, v):
@@ -40,6 +43,14 @@ def _strided(layout, q, k, v):
     if layout == "padded":
         views = []
         for x in (q, k, v):
+            buf = torch.full((B, H, S, D + 64), float("nan"), dtype=x.dtype)
+            buf[..., :D] = x
+            views.append(buf.to(DEV)[..., :D])
+        return views, (q, k, v)
+    if layout == "mixed":
+        q_view = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)  # rows H * D apart
+        views = [q_view]
+        for x in (k, v):  # rows D + 64 apart
             buf = torch.full((B, H, S, D + 64), float("nan"), dtype=x.dtype)
             buf[..., :D] = x
             views.append(buf.to(DEV)[..., :D])
@@ -83,6 +94,7 @@ def test_strided_equals_contiguous_bitwise(layout, D, dtype):
     ("bshd", 256, "bf16", True, 130),
     ("kv_broadcast", 128, "f16", True, 300),
     ("padded", 64, "f16", False, 129),
+    ("mixed", 256, "f16", True, 161),
 ])
 def test_strided_parity_with_oracle(layout, D, dtype, causal, S):
     B, H = 2, 3
