@@ -828,6 +828,9 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     give[(NH * 16) * 64] = m_run[0];
     give[(NH * 16 + 1) * 64] = l_run[0];
     give[(NH * 16 + 2) * 64] = l_rnd[0];
+    // the barrier is plain s_barrier: this wave's LDS writes must have
+    // completed before the other group reads them
+    wait_vm_lgkm0<63>();
     workgroup_barrier();
     const float m_t = take[(NH * 16) * 64];
     const float l_t = take[(NH * 16 + 1) * 64], lr_t = take[(NH * 16 + 2) * 64];

@@ -152,7 +152,8 @@ __device__ __forceinline__ void tile_load_offsets8(int wave, int lane, uint32_t 
   }
 }
 
-// s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding; expcnt not waited).
+// s_waitcnt with vmcnt(N) and lgkmcnt(0) (gfx9 encoding; expcnt not waited;
+// N = 63 leaves the vector memory counter alone).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -162,6 +163,8 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // x made wave-uniform (scalar register); x must already be equal in all lanes.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// s_barrier alone: it does not wait for this wave's memory operations, so
+// LDS writes another wave reads after it need a wait_vm_lgkm0 first.
 __device__ __forceinline__ void workgroup_barrier() {
   __asm__ volatile("s_barrier" ::: "memory");
 }
