@@ -39,6 +39,9 @@
 // the split-KV kernels are described in fa2_tile.h.
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "fa2_plan.h"
 #include "fa2_tile.h"
@@ -408,7 +411,8 @@ template <int D, int DT, bool CAUSAL, bool STRIDED, bool ALT>
 __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPerSimd)) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int S, float c /* scale * log2(e) */, int pair_split, Strides st, KeySplit ks) {
+    int S, float c /* scale * log2(e) */, int pair_split, Strides st, KeySplit ks, int tk_from,
+    unsigned int* __restrict__ tk) {
   using SH = Shape<D, ALT>;
   constexpr int RB = SH::kRB, Bc = SH::kBc, Br = SH::kBr;
   constexpr int CPR = SH::kChunksPerRow, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
@@ -445,9 +449,24 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
   // a light tile beside its heavy first one.
   // Under a key split the grid's x dimension runs over work items instead,
   // each one key chunk (of ct tiles from tile t0) of one query tile.
+  // With tk (multi-round grids), the workgroups from tk_from on take their
+  // place in that order from the counter instead of from blockIdx: in the
+  // order they start, so that the XCDs that run faster take more of the
+  // short tiles at the end. The last of them wraps the counter back to 0.
   const int n_bh = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int bh = lin % n_bh;
+  int lin_t = lin;
+  if (lin >= tk_from) {
+    const int n_wg = (int)(gridDim.x * gridDim.y * gridDim.z);
+    unsigned int* const got = (unsigned int*)smem;  // before the prologue's loads
+    if (threadIdx.x == 0) *got = atomicInc(tk, (unsigned int)(n_wg - tk_from - 1));
+    wait_vm_lgkm0<63>();
+    workgroup_barrier();
+    lin_t = tk_from + wave_uniform((int)*got);
+    wait_vm_lgkm0<63>();
+    workgroup_barrier();
+  }
+  const int bh = lin_t % n_bh;
   FA2_TL(lin, 0, FA2_TL_NOW());
   FA2_TL(lin, 4, (unsigned long long)(unsigned)__builtin_amdgcn_s_getreg(0xf804) |
                      ((unsigned long long)(unsigned)__builtin_amdgcn_s_getreg(0xf814) << 32));
@@ -456,7 +475,8 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
     split_item(lin / n_bh, ks, CAUSAL, qt, chunk);
   } else {
     const int n_qt = gridDim.x;
-    qt = (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh : n_qt - 1 - lin / n_bh;
+    qt = (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh
+                                                : n_qt - 1 - lin_t / n_bh;
   }
   const int t0 = chunk * ks.ct;  // first key tile
   // chunks of this query tile (more than one: the rows leave partials)
@@ -910,7 +930,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
 template <int D, int DT, bool CAUSAL, bool ALT>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int S, float scale, const Strides* st, const KeySplit& ks, int n_cu,
-                  hipStream_t stream) {
+                  unsigned int* tk, hipStream_t stream) {
   using SH = Shape<D, ALT>;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
   // work items per (b, h): query tiles, or their key chunks under a split
@@ -924,17 +944,20 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
   const int pair_split = (CAUSAL && ks.ct == 0 && n_qt > 1 && n_wg <= slots)
                              ? (int)(((n_qt + 1) / 2) * (long long)H * B)
                              : 0;
+  // the last quarter of a multi-round grid takes tickets (none under a key
+  // split, whose items are not in longest-first order)
+  const int tk_from = (tk && ks.ct == 0 && n_wg > slots) ? (int)(n_wg - n_wg / 4) : INT32_MAX;
   const Strides cs{(long long)H * S * D, (long long)S * D, D, (long long)H * S * D,
                    (long long)S * D,     D,                 (long long)H * S * D, (long long)S * D,
                    D,                    (long long)H * S * D, (long long)S * D, D};
   if (st)
     fa2_fwd_kernel<D, DT, CAUSAL, true, ALT><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
-        scale * kLog2e, pair_split, *st, ks);
+        scale * kLog2e, pair_split, *st, ks, tk_from, tk);
   else
     fa2_fwd_kernel<D, DT, CAUSAL, false, ALT><<<grid, block, 0, stream>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, S,
-        scale * kLog2e, pair_split, cs, ks);
+        scale * kLog2e, pair_split, cs, ks, tk_from, tk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ks.ct == 0) return err;
   const Strides& os = st ? *st : cs;
@@ -945,37 +968,37 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
 template <int D, bool ALT>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                         void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
-                        const KeySplit& ks, int n_cu, hipStream_t stream) {
+                        const KeySplit& ks, int n_cu, unsigned int* tk, hipStream_t stream) {
   if (dtype == FA2_F16)
     return causal ? launch<D, FA2_F16, true, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
-                                                   stream)
+                                                   tk, stream)
                   : launch<D, FA2_F16, false, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
-                                                    stream);
+                                                    tk, stream);
   return causal ? launch<D, FA2_BF16, true, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
-                                                  stream)
+                                                  tk, stream)
                 : launch<D, FA2_BF16, false, ALT>(q, k, v, o, lse, B, H, S, scale, st, ks, n_cu,
-                                                   stream);
+                                                   tk, stream);
 }
 
 hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k, const void* v,
                       void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
-                      const KeySplit& ks, int n_cu, hipStream_t stream) {
+                      const KeySplit& ks, int n_cu, unsigned int* tk, hipStream_t stream) {
   switch (D) {
     case 64:
       return S >= FA2_D64_LONG_S
                  ? launch_dtype<64, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                          n_cu, stream)
+                                          n_cu, tk, stream)
                  : launch_dtype<64, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                           n_cu, stream);
+                                           n_cu, tk, stream);
     case 128:
       return d128_alt(B, H, S, causal != 0, ks.ct > 0, n_cu)
                  ? launch_dtype<128, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                           n_cu, stream)
+                                           n_cu, tk, stream)
                  : launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st,
-                                            ks, n_cu, stream);
+                                            ks, n_cu, tk, stream);
     default:
       return launch_dtype<256, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                      n_cu, stream);
+                                      n_cu, tk, stream);
   }
 }
 
@@ -985,6 +1008,60 @@ static_assert(Shape<64, true>::kBr == Shape<64>::kBr &&
                   (FA2_D128_ALT == 0 || Shape<128, true>::kBr == Shape<128>::kBr),
               "both tiles of a head dim (where both are used) take the query rows per "
               "workgroup fa2_rows_per_workgroup reports");
+
+// Counters for the tickets of the prefill kernel's last workgroups: one per
+// (device, stream) that has launched a multi-round grid, in this array (its
+// copy on each GPU, zero when the library is loaded; every complete launch
+// leaves its counter at zero). Calls on one stream run one after another and
+// calls on two streams never share a counter. A call being captured into a
+// graph takes none (its launch keeps the fixed order): a graph may be
+// replayed beside eager calls on another stream. In host code `tickets`
+// names a host-side stand-in; ticket_counter() looks up each device's
+// address once.
+constexpr int kTicketSlots = 1024;
+static __device__ __align__(256) unsigned int tickets[kTicketSlots];
+
+namespace {
+
+constexpr int kMaxTicketDevices = 64;
+std::mutex g_ticket_mu;
+unsigned int* g_ticket_base[kMaxTicketDevices] = {};
+int g_ticket_used[kMaxTicketDevices] = {};
+std::map<std::pair<int, uintptr_t>, int> g_ticket_slot;
+
+// The counter for `stream` on the current device, or nullptr (no tickets:
+// the stream is capturing, its state cannot be read, or every slot is taken).
+unsigned int* ticket_counter(hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (cap != hipStreamCaptureStatusNone) return nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxTicketDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_ticket_mu);
+  if (!g_ticket_base[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(tickets)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_ticket_base[dev] = (unsigned int*)p;
+  }
+  const auto key = std::make_pair(dev, (uintptr_t)stream);
+  auto it = g_ticket_slot.find(key);
+  if (it == g_ticket_slot.end()) {
+    if (g_ticket_used[dev] >= kTicketSlots) return nullptr;
+    it = g_ticket_slot.emplace(key, g_ticket_used[dev]++).first;
+  }
+  return g_ticket_base[dev] + it->second;
+}
+
+}  // namespace
 
 extern "C" int fa2_rows_per_workgroup(int D) {
   switch (D) {
@@ -1073,8 +1150,9 @@ int prefill_call(const void* q, const void* k, const void* v, void* o, float* ls
   }
 
   (void)hipGetLastError();  // start from a clean error state
-  const hipError_t err = launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale,
-                                    strides ? &st : nullptr, ks, n_cu, (hipStream_t)stream);
+  const hipError_t err =
+      launch_any(D, dtype, causal, q, k, v, o, lse, B, H, S, scale, strides ? &st : nullptr, ks,
+                 n_cu, ticket_counter((hipStream_t)stream), (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }
 

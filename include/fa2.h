@@ -91,6 +91,15 @@ typedef enum {
  * keeps no per-call state and is safe to call from several threads.
  * Synchronisation: the work is enqueued on `stream` and the call returns
  * without waiting for it. o and lse must not overlap q, k, v or each other.
+ * Work order: on grids of more than two workgroups per compute unit the
+ * last quarter of the workgroups take their query tiles in the order they
+ * start, from a counter the library holds per (device, stream) in its own
+ * device memory (1024 per device; each launch leaves its counter at zero),
+ * so that faster XCDs take more of the short tiles at the end. Calls on one
+ * stream run in order and calls on different streams use different
+ * counters; a call made while `stream` is being captured into a graph, or
+ * once every counter of the device is in use, takes the fixed order
+ * instead. The results do not depend on the order.
  * Arithmetic: products on fp16/bf16 matrix cores with fp32 accumulation;
  * the softmax state (running max, running sum, unnormalised O) is fp32; O
  * is rounded once, to nearest even, into `dtype`.

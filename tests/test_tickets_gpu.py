@@ -1,0 +1,93 @@
+"""The tickets of the prefill kernel's last workgroups, through the C ABI.
+
+On grids of more than one round the last quarter of the workgroups take
+their query tiles in the order they start, from a counter the library keeps
+per (device, stream); a call being captured into a graph takes none and
+keeps the fixed order. Every tile is computed the same way in either order,
+so the results must be bit-identical to the captured call's:
+- for several multi-round shapes, one after another on one stream (each
+  launch must leave its counter at zero for the next, whatever its size);
+- for two streams launching at once, each with its own counter, many times.
+"""
+import pytest
+import torch
+
+import flashattention_tiled_amd as fa
+import workloads as wl
+from gpu_helpers import DEV, announce
+
+pytestmark = pytest.mark.gpu
+
+# (B, H, S, D, dtype): every one more than 2 workgroups per compute unit on
+# 256 units (a multi-round grid), so that the last quarter takes tickets
+SHAPES = [
+    (1, 12, 8192, 128, "f16"),    # 768 query tiles of 128 rows
+    (2, 16, 2304, 256, "bf16"),   # 576, the unpipelined D = 256 tile
+    (1, 40, 4000, 64, "f16"),     # 1280, D = 64
+    (1, 12, 8192, 128, "f16"),    # the first again: its counter must be back at zero
+]
+
+
+def _inputs(B, H, S, D, dt, seed):
+    w = wl.Workload("tickets", B, H, S, D, dt, True)
+    q, k, v = (x.to(DEV) for x in wl.make_qkv(w, seed=seed))
+    return w, q, k, v
+
+
+def _call(w, q, k, v, o, lse, stream):
+    code = fa.FA2_F16 if w.dtype == "f16" else fa.FA2_BF16
+    return fa.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      w.B, w.H, w.S, w.D, 1, w.scale, code, stream)
+
+
+def _fixed_order(w, q, k, v):
+    """O and lse of a captured call (no tickets), from one graph replay."""
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=DEV)
+    assert _call(w, q, k, v, o, lse, torch.cuda.current_stream().cuda_stream) == fa.FA2_OK
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    status = []
+    with torch.cuda.graph(graph):
+        status.append(_call(w, q, k, v, o, lse, torch.cuda.current_stream().cuda_stream))
+    assert status == [fa.FA2_OK]
+    o.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    return o.clone(), lse.clone()
+
+
+def test_tickets_match_fixed_order_one_stream():
+    for i, (B, H, S, D, dt) in enumerate(SHAPES):
+        announce(f"tickets one stream B={B} H={H} S={S} D={D} {dt}")
+        w, q, k, v = _inputs(B, H, S, D, dt, seed=50 + i)
+        o_ref, lse_ref = _fixed_order(w, q, k, v)
+        for rep in range(3):
+            o = torch.full_like(q, float("nan"))
+            lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+            assert _call(w, q, k, v, o, lse, torch.cuda.current_stream().cuda_stream) == fa.FA2_OK
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref), f"{(B, H, S, D, dt)} call {rep}: O differs"
+            assert torch.equal(lse, lse_ref), f"{(B, H, S, D, dt)} call {rep}: lse differs"
+
+
+def test_tickets_two_streams_at_once():
+    announce("tickets on two streams at once")
+    w, q, k, v = _inputs(1, 12, 8192, 128, "f16", seed=60)
+    w2, q2, k2, v2 = _inputs(1, 12, 8192, 128, "f16", seed=61)
+    ref = _fixed_order(w, q, k, v)
+    ref2 = _fixed_order(w2, q2, k2, v2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    torch.cuda.synchronize()
+    for _ in range(8):
+        o, lse = torch.empty_like(q), torch.empty((1, 12, 8192), dtype=torch.float32, device=DEV)
+        o2, lse2 = torch.empty_like(q2), torch.empty((1, 12, 8192), dtype=torch.float32, device=DEV)
+        torch.cuda.synchronize()  # the outputs exist before either stream writes them
+        assert _call(w, q, k, v, o, lse, s1.cuda_stream) == fa.FA2_OK
+        assert _call(w2, q2, k2, v2, o2, lse2, s2.cuda_stream) == fa.FA2_OK
+        outs.append((o, lse, o2, lse2))
+    torch.cuda.synchronize()
+    for i, (o, lse, o2, lse2) in enumerate(outs):
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"stream 1, round {i}"
+        assert torch.equal(o2, ref2[0]) and torch.equal(lse2, ref2[1]), f"stream 2, round {i}"
