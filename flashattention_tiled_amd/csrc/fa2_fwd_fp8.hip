@@ -113,7 +113,8 @@ template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
     const unsigned char* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int S,
-    float c /* scale * log2(e) * q_descale * k_descale */, float v_mult, int pair_split) {
+    float c /* scale * log2(e) * q_descale * k_descale */, float v_mult, int pair_split,
+    int tk_from, unsigned int* __restrict__ tk) {
   using SH = Fp8Shape<D>;
   constexpr int Br = SH::kBr, Bc = SH::kBc, TB = SH::kTileBytes, LPW = SH::kLoadsPerWave;
   constexpr int NKB = Bc / 32, NKS = SH::kKSteps, NDB = D / 32;
@@ -127,13 +128,25 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
 
   // workgroup -> (query tile, batch * head): the 16-bit kernel's order
   // (longest causal tiles first, a head's tiles H * B apart in launch order,
-  // and the second half ascending when the grid is resident at once)
+  // the second half ascending when the grid is resident at once, and the
+  // last quarter of a multi-round grid by ticket, in the order they start)
   const int n_bh = gridDim.y * gridDim.z;
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int bh = lin % n_bh;
+  int lin_t = lin;
+  if (lin >= tk_from) {
+    const int n_wg = (int)(gridDim.x * gridDim.y * gridDim.z);
+    unsigned int* const got = (unsigned int*)smem;  // before the prologue's loads
+    if (threadIdx.x == 0) *got = atomicInc(tk, (unsigned int)(n_wg - tk_from - 1));
+    wait_vm_lgkm0<63>();
+    workgroup_barrier();
+    lin_t = tk_from + wave_uniform((int)*got);
+    wait_vm_lgkm0<63>();
+    workgroup_barrier();
+  }
+  const int bh = lin_t % n_bh;
   const int n_qt = gridDim.x;
   const int qt =
-      (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh : n_qt - 1 - lin / n_bh;
+      (pair_split > 0 && lin >= pair_split) ? (lin - pair_split) / n_bh : n_qt - 1 - lin_t / n_bh;
   const int q0 = qt * Br;
   const int wave_row0 = q0 + wave * 32;
   const size_t head = (size_t)bh * (size_t)S * D;
@@ -375,30 +388,35 @@ __global__ __launch_bounds__(256, 2) void fa2_fwd_fp8_kernel(
 
 template <int D, int DT, bool CAUSAL>
 hipError_t launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int S, float c, float v_mult, int n_cu, hipStream_t stream) {
+                      int H, int S, float c, float v_mult, int n_cu, unsigned int* tk,
+                      hipStream_t stream) {
   using SH = Fp8Shape<D>;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
   const long long slots = (long long)n_cu * 2;  // two 4-wave workgroups per compute unit
   const long long n_wg = (long long)n_qt * H * B;
   const int pair_split =
       (CAUSAL && n_qt > 1 && n_wg <= slots) ? (int)(((n_qt + 1) / 2) * (long long)H * B) : 0;
+  const int tk_from = (tk && n_wg > slots) ? (int)(n_wg - n_wg / 4) : INT32_MAX;
   fa2_fwd_fp8_kernel<D, DT, CAUSAL><<<dim3((unsigned)n_qt, (unsigned)H, (unsigned)B),
                                       dim3(SH::kThreads), 0, stream>>>(
       (const unsigned char*)q, (const unsigned char*)k, (const unsigned char*)v, (uint16_t*)o, lse,
-      S, c, v_mult, pair_split);
+      S, c, v_mult, pair_split, tk_from, tk);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_fp8_any(int dtype, int causal, const void* q, const void* k, const void* v,
                           void* o, float* lse, int B, int H, int S, float c, float v_mult,
-                          int n_cu, hipStream_t stream) {
+                          int n_cu, unsigned int* tk, hipStream_t stream) {
   if (dtype == FA2_F16)
-    return causal ? launch_fp8<D, FA2_F16, true>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, stream)
-                  : launch_fp8<D, FA2_F16, false>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu,
+    return causal ? launch_fp8<D, FA2_F16, true>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, tk,
+                                                 stream)
+                  : launch_fp8<D, FA2_F16, false>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, tk,
                                                   stream);
-  return causal ? launch_fp8<D, FA2_BF16, true>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, stream)
-                : launch_fp8<D, FA2_BF16, false>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, stream);
+  return causal ? launch_fp8<D, FA2_BF16, true>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, tk,
+                                                stream)
+                : launch_fp8<D, FA2_BF16, false>(q, k, v, o, lse, B, H, S, c, v_mult, n_cu, tk,
+                                                 stream);
 }
 
 }  // namespace
@@ -433,12 +451,13 @@ extern "C" int fa2_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   const int dev = fa2_host::check_device(&n_cu);
   if (dev != FA2_OK) return dev;
   (void)hipGetLastError();
+  unsigned int* const tk = ticket_counter((hipStream_t)stream);
   const hipError_t err =
       D == 64    ? launch_fp8_any<64>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale, n_cu,
-                                      (hipStream_t)stream)
+                                      tk, (hipStream_t)stream)
       : D == 128 ? launch_fp8_any<128>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale,
-                                       n_cu, (hipStream_t)stream)
+                                       n_cu, tk, (hipStream_t)stream)
                  : launch_fp8_any<256>(dtype, causal, q, k, v, o, lse, B, H, S, c, v_descale,
-                                       n_cu, (hipStream_t)stream);
+                                       n_cu, tk, (hipStream_t)stream);
   return err == hipSuccess ? FA2_OK : FA2_ERR_LAUNCH;
 }

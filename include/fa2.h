@@ -333,6 +333,8 @@ int fa2_fwd_splitkv_noalloc(const void *q, const void *k, const void *v, void *o
  * o         (B, H, S, D) contiguous, `dtype` (FA2_F16 or FA2_BF16), the
  *           output's element type only; 16-byte aligned.
  * lse, B, H, S, causal, scale, stream as for fa2_fwd; D is 64, 128 or 256.
+ * Ownership, synchronisation and work order (the tickets of a multi-round
+ * grid's last workgroups, from the same per-stream counters) as for fa2_fwd.
  *
  * Arithmetic: S = Q K^T and O~ = P V on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x
  * e4m3, fp32 accumulation; the instruction's internal sum is not exact

@@ -7,7 +7,8 @@ keeps the fixed order. Every tile is computed the same way in either order,
 so the results must be bit-identical to the captured call's:
 - for several multi-round shapes, one after another on one stream (each
   launch must leave its counter at zero for the next, whatever its size);
-- for two streams launching at once, each with its own counter, many times.
+- for two streams launching at once, each with its own counter, many times;
+- for the FP8 prefill, which takes tickets from the same counters.
 """
 import pytest
 import torch
@@ -91,3 +92,35 @@ def test_tickets_two_streams_at_once():
     for i, (o, lse, o2, lse2) in enumerate(outs):
         assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"stream 1, round {i}"
         assert torch.equal(o2, ref2[0]) and torch.equal(lse2, ref2[1]), f"stream 2, round {i}"
+
+
+def test_fp8_tickets_match_fixed_order():
+    B, H, S, D = 1, 12, 8192, 128  # 768 query tiles
+    announce(f"FP8 tickets B={B} H={H} S={S} D={D}")
+    w = wl.Workload("tickets_fp8", B, H, S, D, "f16", True)
+    q, k, v = (x.to(DEV) for x in wl.make_qkv_fp8(w, seed=70))
+    dq, dk, dv = wl.fp8_descales(w)
+
+    def call(o, lse, stream):
+        return fa.fa2_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, S, D, 1, w.scale, dq, dk, dv, fa.FA2_F16, stream)
+
+    o_ref = torch.empty((B, H, S, D), dtype=torch.float16, device=DEV)
+    lse_ref = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    assert call(o_ref, lse_ref, torch.cuda.current_stream().cuda_stream) == fa.FA2_OK
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    status = []
+    with torch.cuda.graph(graph):
+        status.append(call(o_ref, lse_ref, torch.cuda.current_stream().cuda_stream))
+    assert status == [fa.FA2_OK]
+    o_ref.fill_(float("nan"))
+    graph.replay()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o = torch.full_like(o_ref, float("nan"))
+        lse = torch.full_like(lse_ref, float("nan"))
+        assert call(o, lse, torch.cuda.current_stream().cuda_stream) == fa.FA2_OK
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"FP8 call {rep}: O differs from the fixed order"
+        assert torch.equal(lse, lse_ref), f"FP8 call {rep}: lse differs from the fixed order"
