@@ -932,6 +932,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
                   int H, int S, float scale, const Strides* st, const KeySplit& ks, int n_cu,
                   unsigned int* tk, hipStream_t stream) {
   using SH = Shape<D, ALT>;
+  constexpr bool ALT_KG = SH::kKeyGroups > 1;
   const int n_qt = (S + SH::kBr - 1) / SH::kBr;
   // work items per (b, h): query tiles, or their key chunks under a split
   const int n_x = (int)split_items_per_head(ks, n_qt, CAUSAL);
@@ -945,8 +946,12 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
                              ? (int)(((n_qt + 1) / 2) * (long long)H * B)
                              : 0;
   // the last quarter of a multi-round grid takes tickets (none under a key
-  // split, whose items are not in longest-first order)
-  const int tk_from = (tk && ks.ct == 0 && n_wg > slots) ? (int)(n_wg - n_wg / 4) : INT32_MAX;
+  // split, whose items are not in longest-first order, nor on the key-group
+  // tile: one workgroup per unit exposes the ticket's latency, and the
+  // in-order dispatch already gives each freed unit the longest tile left on
+  // its XCD)
+  const int tk_from =
+      (tk && !ALT_KG && ks.ct == 0 && n_wg > slots) ? (int)(n_wg - n_wg / 4) : INT32_MAX;
   const Strides cs{(long long)H * S * D, (long long)S * D, D, (long long)H * S * D,
                    (long long)S * D,     D,                 (long long)H * S * D, (long long)S * D,
                    D,                    (long long)H * S * D, (long long)S * D, D};
