@@ -407,7 +407,7 @@ struct Strides {
   long long qb, qh, qs, kb, kh, ks, vb, vh, vs, ob, oh, os;
 };
 
-template <int D, int DT, bool CAUSAL, bool STRIDED, bool ALT>
+template <int D, int DT, bool CAUSAL, bool STRIDED, int ALT>
 __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPerSimd)) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
@@ -927,7 +927,7 @@ __global__ __launch_bounds__((Shape<D, ALT>::kThreads), (Tile<D, ALT>::kWavesPer
 // Launch the kernel over (B, H, S); `st` gives the strides of a strided call
 // (nullptr: contiguous tensors), `ks` a key split (ct = 0: none), whose
 // merge follows on the same stream.
-template <int D, int DT, bool CAUSAL, bool ALT>
+template <int D, int DT, bool CAUSAL, int ALT>
 hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int S, float scale, const Strides* st, const KeySplit& ks, int n_cu,
                   unsigned int* tk, hipStream_t stream) {
@@ -970,7 +970,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o, float* l
                                CAUSAL ? ks.row0 : 0, ks.n_split, os.ob, os.oh, os.os, stream);
 }
 
-template <int D, bool ALT>
+template <int D, int ALT>
 hipError_t launch_dtype(int dtype, int causal, const void* q, const void* k, const void* v,
                         void* o, float* lse, int B, int H, int S, float scale, const Strides* st,
                         const KeySplit& ks, int n_cu, unsigned int* tk, hipStream_t stream) {
@@ -991,10 +991,13 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
   switch (D) {
     case 64:
       return S >= FA2_D64_LONG_S
-                 ? launch_dtype<64, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                          n_cu, tk, stream)
-                 : launch_dtype<64, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
-                                           n_cu, tk, stream);
+                 ? launch_dtype<64, 1>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                       n_cu, tk, stream)
+             : d64_kg(B, H, S, causal != 0, ks.ct > 0, n_cu)
+                 ? launch_dtype<64, 2>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                       n_cu, tk, stream)
+                 : launch_dtype<64, 0>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                                       n_cu, tk, stream);
     case 128:
       return d128_alt(B, H, S, causal != 0, ks.ct > 0, n_cu)
                  ? launch_dtype<128, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
@@ -1009,7 +1012,7 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
 
 }  // namespace
 
-static_assert(Shape<64, true>::kBr == Shape<64>::kBr &&
+static_assert(Shape<64, 1>::kBr == Shape<64>::kBr && Shape<64, 2>::kBr == Shape<64>::kBr &&
                   (FA2_D128_ALT == 0 || Shape<128, true>::kBr == Shape<128>::kBr),
               "both tiles of a head dim (where both are used) take the query rows per "
               "workgroup fa2_rows_per_workgroup reports");

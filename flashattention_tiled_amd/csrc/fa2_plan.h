@@ -48,16 +48,17 @@ namespace {
 // The defaults are the best of a sweep over these values on the benchmark
 // shapes (flashattention_tiled_amd/tune.py); FA2_TILE_D<D> overrides one, as
 // "waves, row blocks, keys, waves per SIMD, load spacing[, stages[,
-// pipelined[, key groups]]]". D = 64 and D = 128 have a second (ALT)
-// configuration. D = 64's is for sequences of at least FA2_D64_LONG_S:
-// 32-key tiles at four waves per SIMD, 2-4% faster there and up to 20%
-// slower on short sequences. D = 128's is for causal grids whose workgroups
-// of the main tile are all resident at once (d128_alt): there the longest
-// query tiles set the time, run at one wave per SIMD once their compute
-// unit's other workgroup is done (or from the start, at one workgroup per
-// unit). The ALT tile splits each query tile's keys between two groups of
-// four waves, one workgroup per unit, so that every query tile runs at two
-// waves per SIMD to its end and the units take the tiles longest first.
+// pipelined[, key groups]]]". D = 64 and D = 128 have other (ALT)
+// configurations. D = 64's first (ALT 1) is for sequences of at least
+// FA2_D64_LONG_S: 32-key tiles at four waves per SIMD, 2-4% faster there and
+// up to 20% slower on short sequences. The key-group tiles (D = 128's ALT 1,
+// D = 64's ALT 2) are for causal grids whose workgroups of the main tile are
+// all resident at once (d128_alt, d64_kg): there the longest query tiles set
+// the time, run at one wave per SIMD once their compute unit's other
+// workgroup is done (or from the start, at one workgroup per unit). These
+// tiles split each query tile's keys between two groups of four waves, one
+// workgroup per unit, so that every query tile runs at two waves per SIMD to
+// its end and the units take the tiles longest first.
 template <int W, int RB, int BC, int WPS, int LE, int NST = 2, int PIPE = 1, int KG = 1>
 struct TileCfg {
   static constexpr int kWaves = W, kRowBlocks = RB, kBc = BC, kWavesPerSimd = WPS, kLoadEvery = LE,
@@ -72,6 +73,9 @@ struct TileCfg {
 #ifndef FA2_D64_LONG_S
 #define FA2_D64_LONG_S 8192
 #endif
+#ifndef FA2_TILE_D64_KG
+#define FA2_TILE_D64_KG 8, 1, 64, 2, 1, 2, 1, 2
+#endif
 #ifndef FA2_TILE_D128
 #define FA2_TILE_D128 4, 1, 64, 2, 2
 #endif
@@ -81,14 +85,15 @@ struct TileCfg {
 #ifndef FA2_TILE_D256
 #define FA2_TILE_D256 4, 1, 32, 2, 1, 2, 0
 #endif
-template <int D, bool ALT = false> struct Tile;
+template <int D, int ALT = 0> struct Tile;
 template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};
-template <> struct Tile<64, true> : TileCfg<FA2_TILE_D64_LONG> {};
+template <> struct Tile<64, 1> : TileCfg<FA2_TILE_D64_LONG> {};
+template <> struct Tile<64, 2> : TileCfg<FA2_TILE_D64_KG> {};
 template <> struct Tile<128> : TileCfg<FA2_TILE_D128> {};
 template <> struct Tile<128, true> : TileCfg<FA2_TILE_D128_ALT> {};
 template <> struct Tile<256> : TileCfg<FA2_TILE_D256> {};
 
-template <int D, bool ALT = false> struct Shape {
+template <int D, int ALT = 0> struct Shape {
   static constexpr int kWaves = Tile<D, ALT>::kWaves;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kKeyGroups = Tile<D, ALT>::kKeyGroups;
@@ -316,6 +321,16 @@ bool d128_alt(int B, int H, int S, bool causal, bool split, int n_cu) {
   if (FA2_D128_ALT == 0 || split) return false;
   if (FA2_D128_ALT == 2) return true;
   const long long slots = (long long)n_cu * Tile<128>::kWavesPerSimd * 4 / SH::kWaves;
+  const long long n_wg = (long long)((S + SH::kBr - 1) / SH::kBr) * B * H;
+  return causal && n_wg >= n_cu && n_wg <= slots;
+}
+
+// The same rule for the D = 64 key-group tile (below FA2_D64_LONG_S, where
+// the long-sequence tile takes over).
+bool d64_kg(int B, int H, int S, bool causal, bool split, int n_cu) {
+  using SH = Shape<64>;
+  if (split || S >= FA2_D64_LONG_S) return false;
+  const long long slots = (long long)n_cu * Tile<64>::kWavesPerSimd * 4 / SH::kWaves;
   const long long n_wg = (long long)((S + SH::kBr - 1) / SH::kBr) * B * H;
   return causal && n_wg >= n_cu && n_wg <= slots;
 }

@@ -1,9 +1,10 @@
-"""The D = 128 tile that splits each query tile's keys between two wave
-groups (merged through LDS), against the fp64 oracle on every output.
+"""The D = 128 and D = 64 tiles that split each query tile's keys between
+two wave groups (merged through LDS), against the fp64 oracle on every output.
 
-fa2_fwd takes it for causal D = 128 grids whose main-tile workgroups are all
+fa2_fwd takes them for causal grids whose main-tile workgroups are all
 resident at once with at least one per compute unit (256 to 512 query tiles
-of 128 rows on the 256 units of an MI355X). The cases cover the split at
+of 128 rows on the 256 units of an MI355X; D = 64 below its long-sequence
+tile's S). The cases cover the split at
 every query tile, including the first (whose keys all go to the second
 group), ragged sequence ends inside a group's last tile, an odd number of
 key tiles (the groups run different numbers of tiles), both dtypes, a
@@ -24,7 +25,7 @@ from gpu_helpers import DEV, announce, assert_parity, oracle_full
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # (B, H, S, dtype, scale sign): query tiles = ceil(S / 128) * B * H
+    # (B, H, S, dtype, scale sign[, D]): query tiles = ceil(S / 128) * B * H
     (1, 40, 1000, "f16", 1),     # 320 tiles, ragged end inside a key tile
     (2, 8, 4000, "bf16", 1),     # 512 tiles, 63 key tiles per long row block
     (1, 4, 8192, "f16", 1),      # 256 tiles: one long head per 64 units
@@ -33,15 +34,20 @@ CASES = [
     (1, 32, 2048, "f16", 1),     # 512 tiles: the LLM layer's attention
     (1, 30, 1900, "bf16", 1),    # 450 tiles, 15 per head, ragged end
     (2, 16, 1700, "f16", -1),    # 448 tiles, 14 per head, ragged end, negative scale
+    (2, 16, 1024, "f16", 1, 64),    # D = 64: 256 tiles
+    (1, 32, 2048, "bf16", 1, 64),   # D = 64: 512 tiles
+    (1, 20, 1700, "f16", -1, 64),   # D = 64: 280 tiles, ragged end, negative scale
+    (1, 16, 4097, "bf16", 1, 64),   # D = 64: 528 > 512 tiles, the main tile beside it
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_key_groups_every_row(case):
-    B, H, S, dt, sign = case
-    w = wl.Workload("key_groups", B, H, S, 128, dt, True)
-    scale = sign / math.sqrt(128)
-    announce(f"key groups B={B} H={H} S={S} {dt} scale={scale:+.4f}")
+    B, H, S, dt, sign = case[:5]
+    D = case[5] if len(case) > 5 else 128
+    w = wl.Workload("key_groups", B, H, S, D, dt, True)
+    scale = sign / math.sqrt(D)
+    announce(f"key groups B={B} H={H} S={S} D={D} {dt} scale={scale:+.4f}")
     q, k, v = wl.make_qkv(w, seed=S + H)
     # fa2_fwd itself (attention() may take the key split of fa2_fwd_balanced)
     o, lse = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=scale,
@@ -70,10 +76,11 @@ def test_key_groups_q_rows_apart_from_kv():
     assert_parity(o.cpu(), lse.cpu(), o_ref, lse_ref, "bf16", "key groups Q stride apart")
 
 
-def test_key_groups_strided():
+@pytest.mark.parametrize("D", [128, 64])
+def test_key_groups_strided(D):
     """Q, K and V as views into one packed (B, S, 3, H, D) projection."""
-    B, H, S, D = 1, 48, 700, 128
-    announce(f"key groups strided B={B} H={H} S={S}")
+    B, H, S = 1, 48, 700
+    announce(f"key groups strided B={B} H={H} S={S} D={D}")
     w = wl.Workload("key_groups_strided", B, H, S, D, "f16", True)
     q, k, v = wl.make_qkv(w, seed=7)
     packed = torch.empty((B, S, 3, H, D), dtype=torch.float16, device=DEV)
