@@ -1000,12 +1000,12 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
                                        n_cu, tk, stream);
     case 128:
       return d128_alt(B, H, S, causal != 0, ks.ct > 0, n_cu)
-                 ? launch_dtype<128, true>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+                 ? launch_dtype<128, 1>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
                                            n_cu, tk, stream)
-                 : launch_dtype<128, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st,
+                 : launch_dtype<128, 0>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st,
                                             ks, n_cu, tk, stream);
     default:
-      return launch_dtype<256, false>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
+      return launch_dtype<256, 0>(dtype, causal, q, k, v, o, lse, B, H, S, scale, st, ks,
                                       n_cu, tk, stream);
   }
 }
@@ -1013,7 +1013,7 @@ hipError_t launch_any(int D, int dtype, int causal, const void* q, const void* k
 }  // namespace
 
 static_assert(Shape<64, 1>::kBr == Shape<64>::kBr && Shape<64, 2>::kBr == Shape<64>::kBr &&
-                  (FA2_D128_ALT == 0 || Shape<128, true>::kBr == Shape<128>::kBr),
+                  (FA2_D128_ALT == 0 || Shape<128, 1>::kBr == Shape<128>::kBr),
               "both tiles of a head dim (where both are used) take the query rows per "
               "workgroup fa2_rows_per_workgroup reports");
 

@@ -90,7 +90,7 @@ template <> struct Tile<64> : TileCfg<FA2_TILE_D64> {};
 template <> struct Tile<64, 1> : TileCfg<FA2_TILE_D64_LONG> {};
 template <> struct Tile<64, 2> : TileCfg<FA2_TILE_D64_KG> {};
 template <> struct Tile<128> : TileCfg<FA2_TILE_D128> {};
-template <> struct Tile<128, true> : TileCfg<FA2_TILE_D128_ALT> {};
+template <> struct Tile<128, 1> : TileCfg<FA2_TILE_D128_ALT> {};
 template <> struct Tile<256> : TileCfg<FA2_TILE_D256> {};
 
 template <int D, int ALT = 0> struct Shape {
@@ -245,7 +245,7 @@ constexpr double kSplitMargin = 1.5;
 // and at least all its work at the whole GPU's rate; the split is taken
 // when the time it saves by that estimate beats the merge's cost by
 // kSplitMargin.
-template <int D, bool ALT>
+template <int D, int ALT>
 KeySplit plan_split_for(int B, int H, int S, bool causal, int n_cu) {
   using SH = Shape<D, ALT>;
   KeySplit ks{};
@@ -338,10 +338,10 @@ bool d64_kg(int B, int H, int S, bool causal, bool split, int n_cu) {
 KeySplit plan_split(int D, int B, int H, int S, bool causal, int n_cu) {
   switch (D) {
     case 64:
-      return S >= FA2_D64_LONG_S ? plan_split_for<64, true>(B, H, S, causal, n_cu)
-                                 : plan_split_for<64, false>(B, H, S, causal, n_cu);
-    case 128: return plan_split_for<128, false>(B, H, S, causal, n_cu);
-    default: return plan_split_for<256, false>(B, H, S, causal, n_cu);
+      return S >= FA2_D64_LONG_S ? plan_split_for<64, 1>(B, H, S, causal, n_cu)
+                                 : plan_split_for<64, 0>(B, H, S, causal, n_cu);
+    case 128: return plan_split_for<128, 0>(B, H, S, causal, n_cu);
+    default: return plan_split_for<256, 0>(B, H, S, causal, n_cu);
   }
 }
 
