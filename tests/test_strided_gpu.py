@@ -174,3 +174,26 @@ def test_strided_d64_long_sequence_tile():
     o_c, lse_c = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o_s, o_c) and torch.equal(lse_s, lse_c)
+
+
+@pytest.mark.parametrize("layout", ["packed_qkv", "mixed"])
+def test_strided_multi_round_grid(layout):
+    """A grid of three workgroups per compute unit (768 query tiles), whose
+    last quarter takes tickets: strided views bitwise equal to the
+    contiguous call, and sampled rows against the oracle."""
+    B, H, S, D = 1, 12, 8192, 128
+    announce(f"strided multi-round {layout} B={B} H={H} S={S}")
+    w = wl.Workload("strided", B, H, S, D, "f16", True)
+    q, k, v = wl.make_qkv(w, seed=13)
+    views, _ = _strided(layout, q, k, v)
+    o_s, lse_s = fa.attention(*views, causal=True, scale=w.scale, balanced=False,
+                              out=_out_like(layout, B, H, S, D, q.dtype))
+    o_c, lse_c = fa.attention(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, scale=w.scale,
+                              balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_c) and torch.equal(lse_s, lse_c)
+    rows = sample_rows(B, H, S, seed=4)
+    o_ref, lse_ref = oracle_rows(q, k, v, rows, True, w.scale)
+    o_rows = o_s.contiguous().reshape(-1, D).cpu()[torch.from_numpy(rows)]
+    lse_rows = lse_s.reshape(-1).cpu()[torch.from_numpy(rows)]
+    assert_parity(o_rows, lse_rows, o_ref, lse_ref, "f16", f"strided multi-round {layout}")
