@@ -39,6 +39,7 @@
 // the split-KV kernels are described in fa2_tile.h.
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -1021,7 +1022,8 @@ static_assert(Shape<64, 1>::kBr == Shape<64>::kBr && Shape<64, 2>::kBr == Shape<
 // (device, stream) that has launched a multi-round grid, in this array (its
 // copy on each GPU, zero when the library is loaded; every complete launch
 // leaves its counter at zero). Calls on one stream run one after another and
-// calls on two streams never share a counter. A call being captured into a
+// calls on two streams (hipStreamPerThread counts as one per host thread)
+// never share a counter. A call being captured into a
 // graph takes none (its launch keeps the fixed order): a graph may be
 // replayed beside eager calls on another stream. In host code `tickets`
 // names a host-side stand-in; ticket_counter() looks up each device's
@@ -1060,7 +1062,12 @@ unsigned int* ticket_counter(hipStream_t stream) {
     }
     g_ticket_base[dev] = (unsigned int*)p;
   }
-  const auto key = std::make_pair(dev, (uintptr_t)stream);
+  // hipStreamPerThread names a different stream in each host thread: key it
+  // by a number each thread draws once (never reused, unlike a thread's id)
+  static std::atomic<uintptr_t> next_thread{1};
+  static thread_local const uintptr_t this_thread = next_thread.fetch_add(1);
+  const uintptr_t id = stream == hipStreamPerThread ? ~this_thread : (uintptr_t)stream;
+  const auto key = std::make_pair(dev, id);
   auto it = g_ticket_slot.find(key);
   if (it == g_ticket_slot.end()) {
     if (g_ticket_used[dev] >= kTicketSlots) return nullptr;

@@ -97,7 +97,8 @@ typedef enum {
  * device memory (1024 per device; each launch leaves its counter at zero),
  * so that faster XCDs take more of the short tiles at the end. Calls on one
  * stream run in order and calls on different streams use different
- * counters; a call made while `stream` is being captured into a graph, or
+ * counters (hipStreamPerThread counting as a stream of its own in each host
+ * thread); a call made while `stream` is being captured into a graph, or
  * once every counter of the device is in use, takes the fixed order
  * instead. The results do not depend on the order.
  * Arithmetic: products on fp16/bf16 matrix cores with fp32 accumulation;

@@ -7,7 +7,8 @@ keeps the fixed order. Every tile is computed the same way in either order,
 so the results must be bit-identical to the captured call's:
 - for several multi-round shapes, one after another on one stream (each
   launch must leave its counter at zero for the next, whatever its size);
-- for two streams launching at once, each with its own counter, many times;
+- for two streams launching at once, each with its own counter, many times,
+  and for hipStreamPerThread used by two host threads at once;
 - for the FP8 prefill, which takes tickets from the same counters.
 """
 import pytest
@@ -124,3 +125,38 @@ def test_fp8_tickets_match_fixed_order():
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref), f"FP8 call {rep}: O differs from the fixed order"
         assert torch.equal(lse, lse_ref), f"FP8 call {rep}: lse differs from the fixed order"
+
+
+def test_tickets_per_thread_default_streams():
+    """hipStreamPerThread, one handle naming a different stream in each host
+    thread: two threads launching on it at once get a counter each."""
+    import threading
+
+    per_thread = 2  # hipStreamPerThread
+    announce("tickets on two threads' per-thread streams")
+    w, q, k, v = _inputs(1, 12, 8192, 128, "f16", seed=80)
+    w2, q2, k2, v2 = _inputs(1, 12, 8192, 128, "f16", seed=81)
+    refs = [_fixed_order(w, q, k, v), _fixed_order(w2, q2, k2, v2)]
+    jobs = [(w, q, k, v), (w2, q2, k2, v2)]
+    outs = [[(torch.empty_like(q), torch.empty((1, 12, 8192), dtype=torch.float32, device=DEV))
+             for _ in range(6)] for _ in range(2)]
+    torch.cuda.synchronize()
+    status = [[], []]
+
+    def run(t):
+        wt, qt, kt, vt = jobs[t]
+        for o, lse in outs[t]:
+            status[t].append(_call(wt, qt, kt, vt, o, lse, per_thread))
+        # this thread's per-thread stream ends with the thread: wait for it here
+        torch.cuda.synchronize()
+
+    threads = [threading.Thread(target=run, args=(t,)) for t in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    for t in range(2):
+        assert status[t] == [fa.FA2_OK] * 6, status[t]
+        for i, (o, lse) in enumerate(outs[t]):
+            assert torch.equal(o, refs[t][0]) and torch.equal(lse, refs[t][1]), f"thread {t}, call {i}"
